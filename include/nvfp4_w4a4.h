@@ -1,0 +1,170 @@
+/*
+ * nvfp4_w4a4.h -- C ABI of the MI355X (gfx950) NVFP4 W4A4 hot path.
+ *
+ * The format and the operations follow two pages about the paper
+ * "Why Gated DeltaNet Survives 4-Bit Quantization: NVFP4 W4A4 for the
+ * Recurrent Half of a Hybrid 27B LLM":
+ *   [P1] its arxiv-wiki summary page (sections "접근 방법" = approach,
+ *        "개발자 관점" = developer view),
+ *   [P3] the ta-paperlens explainer "論文解説: Gated DeltaNet はなぜ4bit量子化に
+ *        耐えるのか" (sections "前提1" = what 4-bit rounding is, "前提2" = what
+ *        Gated DeltaNet computes).
+ *
+ * NVFP4 tensor ([P3] 前提1, [P1] 접근 방법): 4-bit E2M1 values (1 sign,
+ * 2 exponent, 1 mantissa bit: magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6), one
+ * OCP E4M3 scale per 16 consecutive elements (set from the block maximum
+ * over 6), and one FP32 scale per tensor.  W4A4: both GEMM operands are in
+ * this format.
+ *
+ * Layouts (all row-major, no padding, no swizzle):
+ *   codes : uint8 [rows][k/2]; element 2j in the low nibble of byte j,
+ *           element 2j+1 in the high nibble; bit 3 of a nibble is the sign.
+ *   scales: uint8 [rows][k/16]; raw OCP E4M3 bytes (never negative, never
+ *           the NaN code 0x7F).
+ *   global: one float on the device, the decode scale g: the value of an
+ *           element is e2m1(code) * e4m3(scale) * g.  Computed from a tensor
+ *           as g = fp32(max|x| / 2688), 2688 = 6 * 448.
+ *   Blocks of 16 run along k, the reduction axis of the GEMM.
+ *
+ * Conventions for every call:
+ *   - All buffers are device memory owned by the caller; the library
+ *     allocates nothing and keeps no state between calls.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls validate
+ *     their arguments on the host, enqueue kernels and return without
+ *     synchronising.  A kernel fault is reported by the next synchronising
+ *     HIP call of the caller.
+ *   - A nonzero return is an nvfp4_status; nothing was enqueued unless the
+ *     status is NVFP4_ERR_LAUNCH.  nvfp4_status_string() names it.
+ *   - Inputs must be finite; that is a precondition and is not checked.
+ *   - Calls that overlap on one stream are ordered by it; buffers shared by
+ *     calls on different streams need the caller's own ordering.
+ */
+#ifndef NVFP4_W4A4_H
+#define NVFP4_W4A4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NVFP4_OK = 0,
+    NVFP4_ERR_INVALID_VALUE = 1, /* null pointer, bad size, k % 16 != 0, ... */
+    NVFP4_ERR_UNSUPPORTED = 2,   /* unknown dtype / mode / epilogue          */
+    NVFP4_ERR_MISALIGNED = 3,    /* a pointer or stride breaks the alignment  */
+    NVFP4_ERR_LAUNCH = 4         /* the HIP runtime refused a launch          */
+} nvfp4_status;
+
+typedef enum {
+    NVFP4_DTYPE_F32 = 0,
+    NVFP4_DTYPE_BF16 = 1
+} nvfp4_dtype;
+
+typedef enum {
+    NVFP4_GLOBAL_COMPUTE = 0, /* g = fp32(max|x| / 2688), written to *global */
+    NVFP4_GLOBAL_GIVEN = 1    /* *global is read as a calibrated static g    */
+} nvfp4_global_mode;
+
+typedef enum {
+    W4A4_EPI_NONE = 0,  /* y                                   */
+    W4A4_EPI_ALPHA = 1, /* exp(-softplus(y)): decay gate        */
+    W4A4_EPI_BETA = 2   /* sigmoid(y): write-strength gate      */
+} w4a4_epilogue;
+
+/*
+ * nvfp4_quantize -- NVFP4 quantisation of a [rows][k] tensor.
+ * Defined by [P3] 前提1 and [P1] 접근 방법 (16-element blocks, E4M3 block
+ * scale from block max / 6, E2M1 values, FP32 per-tensor scale).
+ *
+ *   x          device, [rows][ldx] elements of x_dtype (F32 or BF16); only
+ *              the first k of each row are read.  16-byte aligned; ldx*size
+ *              a multiple of 16 bytes.
+ *   rows, k    rows >= 1, k >= 16, k % 16 == 0.
+ *   ldx        row stride in elements, ldx >= k.
+ *   codes      device, out, [rows][k/2] bytes, 8-byte aligned.
+ *   scales     device, out, [rows][k/16] bytes.
+ *   global     device, one float: written in COMPUTE mode (the tensor's g),
+ *              read in GIVEN mode (must be finite and >= 0).
+ *   mode       nvfp4_global_mode.
+ *
+ * Result, per 16-element block with maximum magnitude m: scale
+ * s = E4M3(m / (6 g)) and codes c = sign(x) | E2M1(|x| / (e4m3(s) g)), each
+ * quotient exact and rounded once to nearest, ties to the even code,
+ * saturating at 448 and 6; s = 0 and magnitude 0 when m = 0 or g = 0.
+ * Bit-exact with this definition on every finite input.
+ * COMPUTE mode enqueues four kernels (init, amax, finalize, quantize);
+ * GIVEN mode one.  x must not overlap the outputs.
+ */
+int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t k,
+                   int64_t ldx, uint8_t* codes, uint8_t* scales,
+                   float* global, int mode, void* stream);
+
+/*
+ * nvfp4_harmonize_group -- rewrite the modules of a fused-GEMM group to one
+ * shared global scale, folding each module's ratio into its block scales.
+ * Defined by [P1] 접근 방법 and 개발자 관점 (the fix for per-module
+ * calibrated checkpoints served by kernels that fuse qkv|z and b|a into one
+ * GEMM) and the abstract on the paper's listing page.
+ *
+ *   scales        device, in/out, [n_total][k/16] E4M3 bytes of the fused
+ *                 weight; module i owns rows [row_offsets[i],
+ *                 row_offsets[i+1]).  The codes are not touched.
+ *   k             k >= 16, k % 16 == 0.
+ *   row_offsets   HOST array of n_modules + 1 increasing values,
+ *                 row_offsets[0] == 0, row_offsets[n_modules] = n_total.
+ *   n_modules     1 .. 64.
+ *   module_globals device, [n_modules] floats g_i (finite, >= 0).
+ *   shared_global device, out, one float: g* = max_i g_i.  Must not
+ *                 overlap module_globals or scales.
+ *
+ * Result: every scale s of module i becomes E4M3(e4m3(s) * g_i / g*),
+ * exact quotient rounded once (ties to even); rows of modules with
+ * g_i == g* are left unchanged.  Afterwards e2m1 * e4m3(s') * g* equals the
+ * module's own dequantised weight up to that one rounding of the scale.
+ * Calling it twice on the same buffer re-folds the scales (not idempotent).
+ */
+int nvfp4_harmonize_group(uint8_t* scales, int64_t k,
+                          const int64_t* row_offsets, int n_modules,
+                          const float* module_globals, float* shared_global,
+                          void* stream);
+
+/*
+ * w4a4_gemm -- Y = (g_a g_b) * A_hat B_hat^T on NVFP4 operands, with an
+ * optional gate epilogue.  The W4A4 linear of [P3] 前提1 / [P1] 접근 방법;
+ * the gates are those of [P3] 前提2 (alpha through softplus and exp, beta
+ * through a sigmoid), in the form alpha = exp(-softplus(y)),
+ * beta = sigmoid(y).
+ *
+ *   a_codes, a_scales, a_global  activations A [m][k] in the layout above
+ *                                (codes 16-byte aligned).
+ *   b_codes, b_scales, b_global  weights B [n][k] (K-major, the same
+ *                                layout; codes 16-byte aligned).
+ *   m, n, k      m, n >= 1, k >= 16, k % 16 == 0.
+ *   out          device, [m][ldo] of out_dtype (F32 or BF16), ldo >= n;
+ *                4-byte aligned.  Must not overlap the inputs.
+ *   epilogue     w4a4_epilogue, applied in fp32 before the store.
+ *
+ * Every A_hat[i][k] = e2m1 * e4m3 and B_hat[j][k] is decoded exactly (the
+ * products are exact in fp16); products are accumulated in fp32; the
+ * global factors multiply the fp32 sum; BF16 output is rounded to nearest
+ * even from that fp32 value.
+ */
+int w4a4_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
+              const float* a_global, int64_t m,
+              const uint8_t* b_codes, const uint8_t* b_scales,
+              const float* b_global, int64_t n, int64_t k,
+              void* out, int out_dtype, int64_t ldo, int epilogue,
+              void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* nvfp4_status_string(int status);
+
+/* ABI version of this header: 1. */
+int nvfp4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_W4A4_H */
