@@ -1,0 +1,204 @@
+"""NVFP4 W4A4 hot path for MI355X (gfx950): Python binding.
+
+A thin ctypes layer over libnvfp4_w4a4.so (C ABI in include/nvfp4_w4a4.h).
+It only marshals arguments: torch tensors provide device memory and the
+current HIP stream; every step of the computation runs in the library's
+HIP kernels.  Importing works without a GPU; calling needs the built library
+and a GPU, and fails loudly otherwise.
+
+    q = quantize(x)                        # NVFP4(codes, scales, global_scale)
+    q = quantize(x, global_scale=g)        # calibrated static global
+    g_star = harmonize_group(scales, k, row_offsets, module_globals)
+    y = gemm(a, b, out_dtype=torch.bfloat16, epilogue="none")
+"""
+import ctypes
+import os
+from collections import namedtuple
+
+import torch
+
+__all__ = ["NVFP4", "quantize", "harmonize_group", "gemm", "library",
+           "LIB_PATH", "NVFP4Error"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                        "libnvfp4_w4a4.so")
+
+# Enumerations of the C ABI.
+DTYPE_F32, DTYPE_BF16 = 0, 1
+GLOBAL_COMPUTE, GLOBAL_GIVEN = 0, 1
+EPILOGUES = {"none": 0, "alpha": 1, "beta": 2}
+
+NVFP4 = namedtuple("NVFP4", ["codes", "scales", "global_scale"])
+NVFP4.__doc__ = """A packed NVFP4 tensor: codes uint8 [rows, k/2] (element 2j
+in the low nibble of byte j), scales uint8 [rows, k/16] (OCP E4M3), and
+global_scale float32 [1] (decode scale: value = e2m1 * e4m3 * g)."""
+
+
+class NVFP4Error(RuntimeError):
+    """A nonzero nvfp4_status returned by the library."""
+
+
+_lib = None
+
+
+def library():
+    """Load libnvfp4_w4a4.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            "libnvfp4_w4a4.so is not built (expected at %s); run "
+            "python -c 'import __graft_entry__; __graft_entry__.build()'"
+            % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.nvfp4_quantize.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, i32, vp]
+    L.nvfp4_quantize.restype = i32
+    L.nvfp4_harmonize_group.argtypes = [vp, i64, ctypes.POINTER(i64), i32,
+                                        vp, vp, vp]
+    L.nvfp4_harmonize_group.restype = i32
+    L.w4a4_gemm.argtypes = [vp, vp, vp, i64, vp, vp, vp, i64, i64, vp, i32,
+                            i64, i32, vp]
+    L.w4a4_gemm.restype = i32
+    L.nvfp4_status_string.argtypes = [i32]
+    L.nvfp4_status_string.restype = ctypes.c_char_p
+    L.nvfp4_abi_version.argtypes = []
+    L.nvfp4_abi_version.restype = i32
+    _lib = L
+    return L
+
+
+def _check(rc, what=""):
+    if rc != 0:
+        raise NVFP4Error(library().nvfp4_status_string(rc).decode() +
+                         (" [%s]" % what if what else ""))
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _device_tensor(t, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError("%s must be a torch tensor on a GPU" % name)
+
+
+def quantize(x, global_scale=None, out=None):
+    """NVFP4-quantise a [rows, k] float32 or bfloat16 GPU tensor.
+
+    global_scale=None: the tensor's own global g = fp32(amax / 2688) is
+    computed on the device (self-calibration).  Otherwise global_scale is a
+    float32 GPU tensor of one element used as given (a calibrated static
+    global).  out=(codes, scales) lets the caller pick the output buffers
+    (for example row slices of a fused weight).  Returns NVFP4.
+    """
+    _device_tensor(x, "x")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit stride along k")
+    if x.dtype == torch.float32:
+        dt = DTYPE_F32
+    elif x.dtype == torch.bfloat16:
+        dt = DTYPE_BF16
+    else:
+        raise ValueError("x must be float32 or bfloat16")
+    rows, k = x.shape
+    # a one-row tensor's row stride is arbitrary (numpy/torch may report 0)
+    ldx = x.stride(0) if rows > 1 else k
+    if out is None:
+        codes = torch.empty((rows, k // 2), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((rows, k // 16), dtype=torch.uint8,
+                             device=x.device)
+    else:
+        codes, scales = out
+        if codes.shape != (rows, k // 2) or scales.shape != (rows, k // 16) \
+                or not codes.is_contiguous() or not scales.is_contiguous():
+            raise ValueError("out buffers have the wrong shape or layout")
+    if global_scale is None:
+        g = torch.empty(1, dtype=torch.float32, device=x.device)
+        mode = GLOBAL_COMPUTE
+    else:
+        _device_tensor(global_scale, "global_scale")
+        if global_scale.dtype != torch.float32 or global_scale.numel() != 1:
+            raise ValueError("global_scale must be one float32")
+        g = global_scale
+        mode = GLOBAL_GIVEN
+    _check(library().nvfp4_quantize(_ptr(x), dt, rows, k, ldx,
+                                    _ptr(codes), _ptr(scales), _ptr(g), mode,
+                                    _stream(x)),
+           "quantize x=%#x dtype=%d rows=%d k=%d ldx=%d codes=%#x "
+           "scales=%#x global=%#x" % (x.data_ptr(), dt, rows, k, ldx,
+                                      codes.data_ptr(), scales.data_ptr(),
+                                      g.data_ptr()))
+    return NVFP4(codes, scales, g)
+
+
+def harmonize_group(scales, k, row_offsets, module_globals,
+                    shared_global=None):
+    """Rewrite the scales of a fused group in place to one shared global.
+
+    scales: uint8 GPU tensor [n_total, k/16]; module i owns rows
+    row_offsets[i]:row_offsets[i+1] (a host sequence of ints starting at 0);
+    module_globals: float32 GPU tensor [n_modules].  Returns the shared
+    global (float32 GPU tensor [1]).
+    """
+    _device_tensor(scales, "scales")
+    _device_tensor(module_globals, "module_globals")
+    n_mod = len(row_offsets) - 1
+    if module_globals.dtype != torch.float32 or \
+            module_globals.numel() != n_mod or \
+            not module_globals.is_contiguous():
+        raise ValueError("module_globals must be float32 [n_modules]")
+    if not scales.is_contiguous() or scales.dtype != torch.uint8 or \
+            scales.shape != (row_offsets[-1], k // 16):
+        raise ValueError("scales must be contiguous uint8 [n_total, k/16]")
+    if shared_global is None:
+        shared_global = torch.empty(1, dtype=torch.float32,
+                                    device=scales.device)
+    offs = (ctypes.c_int64 * (n_mod + 1))(*[int(v) for v in row_offsets])
+    _check(library().nvfp4_harmonize_group(_ptr(scales), k, offs, n_mod,
+                                           _ptr(module_globals),
+                                           _ptr(shared_global),
+                                           _stream(scales)))
+    return shared_global
+
+
+def gemm(a, b, out_dtype=torch.bfloat16, epilogue="none", out=None):
+    """Y = g_a g_b * A_hat B_hat^T for NVFP4 operands a [m, k] and b [n, k]
+    (weights, K-major).  epilogue: "none", "alpha" (exp(-softplus(y))) or
+    "beta" (sigmoid(y)).  Returns a [m, n] float32 or bfloat16 tensor."""
+    ac, as_, ag = a
+    bc, bs, bg = b
+    for t, nm in ((ac, "a.codes"), (as_, "a.scales"), (ag, "a.global_scale"),
+                  (bc, "b.codes"), (bs, "b.scales"), (bg, "b.global_scale")):
+        _device_tensor(t, nm)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % nm)
+    m, k = ac.shape[0], ac.shape[1] * 2
+    n = bc.shape[0]
+    if bc.shape[1] * 2 != k or as_.shape != (m, k // 16) or \
+            bs.shape != (n, k // 16):
+        raise ValueError("operand shapes disagree")
+    if out_dtype == torch.float32:
+        od = DTYPE_F32
+    elif out_dtype == torch.bfloat16:
+        od = DTYPE_BF16
+    else:
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    if epilogue not in EPILOGUES:
+        raise ValueError("epilogue must be one of %s" % sorted(EPILOGUES))
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=ac.device)
+    elif out.dtype != out_dtype or out.dim() != 2 or out.shape != (m, n) \
+            or out.stride(1) != 1:
+        raise ValueError("out has the wrong dtype, shape or layout")
+    _check(library().w4a4_gemm(_ptr(ac), _ptr(as_), _ptr(ag), m, _ptr(bc),
+                               _ptr(bs), _ptr(bg), n, k, _ptr(out), od,
+                               out.stride(0) if m > 1 else n,
+                               EPILOGUES[epilogue],
+                               _stream(ac)))
+    return out

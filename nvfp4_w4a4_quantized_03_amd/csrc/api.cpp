@@ -1,0 +1,145 @@
+// C ABI front end: argument validation on the host, then kernel dispatch.
+// Every check runs before any HIP call, so a rejected call touches no
+// device state (and can be exercised on a machine without a GPU).
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/nvfp4_w4a4.h"
+#include "internal.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+// [lo, lo + len) and [lo2, lo2 + len2) intersect (byte ranges).
+bool overlap(const void* a, int64_t alen, const void* b, int64_t blen) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a);
+  const uintptr_t y = reinterpret_cast<uintptr_t>(b);
+  return x < y + static_cast<uintptr_t>(blen) &&
+         y < x + static_cast<uintptr_t>(alen);
+}
+
+// Sizes whose byte extents stay far below 2^62.
+constexpr int64_t kMaxDim = int64_t(1) << 40;
+
+int status_of(hipError_t e) {
+  return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_abi_version(void) { return 1; }
+
+const char* nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_OK: return "NVFP4_OK";
+    case NVFP4_ERR_INVALID_VALUE:
+      return "NVFP4_ERR_INVALID_VALUE: null pointer, bad size, k not a "
+             "multiple of 16, bad stride or overlapping buffers";
+    case NVFP4_ERR_UNSUPPORTED:
+      return "NVFP4_ERR_UNSUPPORTED: unknown dtype, global mode or epilogue";
+    case NVFP4_ERR_MISALIGNED:
+      return "NVFP4_ERR_MISALIGNED: a pointer or row stride breaks the "
+             "required alignment";
+    case NVFP4_ERR_LAUNCH:
+      return "NVFP4_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
+    default: return "unknown nvfp4 status";
+  }
+}
+
+int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t k,
+                   int64_t ldx, uint8_t* codes, uint8_t* scales,
+                   float* global, int mode, void* stream) {
+  if (!x || !codes || !scales || !global) return NVFP4_ERR_INVALID_VALUE;
+  if (rows < 1 || k < 16 || k % 16 != 0 || ldx < k) return NVFP4_ERR_INVALID_VALUE;
+  if (rows > kMaxDim || ldx > kMaxDim || rows > kMaxDim / ldx)
+    return NVFP4_ERR_INVALID_VALUE;
+  if (rows * (k / 16) > (int64_t(1) << 39)) return NVFP4_ERR_INVALID_VALUE;
+  if (x_dtype != NVFP4_DTYPE_F32 && x_dtype != NVFP4_DTYPE_BF16)
+    return NVFP4_ERR_UNSUPPORTED;
+  if (mode != NVFP4_GLOBAL_COMPUTE && mode != NVFP4_GLOBAL_GIVEN)
+    return NVFP4_ERR_UNSUPPORTED;
+  const int64_t es = x_dtype == NVFP4_DTYPE_F32 ? 4 : 2;
+  if (!aligned(x, 16) || (ldx * es) % 16 != 0 || !aligned(codes, 8) ||
+      !aligned(global, 4))
+    return NVFP4_ERR_MISALIGNED;
+  const int64_t xbytes = ((rows - 1) * ldx + k) * es;
+  const int64_t cbytes = rows * (k / 2), sbytes = rows * (k / 16);
+  if (overlap(x, xbytes, codes, cbytes) || overlap(x, xbytes, scales, sbytes) ||
+      overlap(x, xbytes, global, 4) || overlap(codes, cbytes, scales, sbytes) ||
+      overlap(codes, cbytes, global, 4) || overlap(scales, sbytes, global, 4))
+    return NVFP4_ERR_INVALID_VALUE;
+  return status_of(nvfp4::launch_quantize(x, x_dtype, rows, k, ldx, codes,
+                                          scales, global, mode,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int nvfp4_harmonize_group(uint8_t* scales, int64_t k,
+                          const int64_t* row_offsets, int n_modules,
+                          const float* module_globals, float* shared_global,
+                          void* stream) {
+  if (!scales || !row_offsets || !module_globals || !shared_global)
+    return NVFP4_ERR_INVALID_VALUE;
+  if (k < 16 || k % 16 != 0 || k > kMaxDim) return NVFP4_ERR_INVALID_VALUE;
+  if (n_modules < 1 || n_modules > nvfp4::kMaxModules)
+    return NVFP4_ERR_INVALID_VALUE;
+  if (row_offsets[0] != 0) return NVFP4_ERR_INVALID_VALUE;
+  for (int i = 0; i < n_modules; ++i)
+    if (row_offsets[i + 1] <= row_offsets[i]) return NVFP4_ERR_INVALID_VALUE;
+  const int64_t total_rows = row_offsets[n_modules];
+  if (total_rows > kMaxDim || total_rows > (int64_t(1) << 39) / (k / 16))
+    return NVFP4_ERR_INVALID_VALUE;
+  if (!aligned(module_globals, 4) || !aligned(shared_global, 4))
+    return NVFP4_ERR_MISALIGNED;
+  const int64_t sbytes = total_rows * (k / 16);
+  if (overlap(shared_global, 4, module_globals, 4 * int64_t(n_modules)) ||
+      overlap(shared_global, 4, scales, sbytes) ||
+      overlap(module_globals, 4 * int64_t(n_modules), scales, sbytes))
+    return NVFP4_ERR_INVALID_VALUE;
+  return status_of(nvfp4::launch_harmonize(scales, k, row_offsets, n_modules,
+                                           module_globals, shared_global,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int w4a4_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
+              const float* a_global, int64_t m,
+              const uint8_t* b_codes, const uint8_t* b_scales,
+              const float* b_global, int64_t n, int64_t k,
+              void* out, int out_dtype, int64_t ldo, int epilogue,
+              void* stream) {
+  if (!a_codes || !a_scales || !a_global || !b_codes || !b_scales ||
+      !b_global || !out)
+    return NVFP4_ERR_INVALID_VALUE;
+  if (m < 1 || n < 1 || k < 16 || k % 16 != 0 || ldo < n)
+    return NVFP4_ERR_INVALID_VALUE;
+  if (m > kMaxDim || n > kMaxDim || k > kMaxDim || ldo > kMaxDim ||
+      m > kMaxDim / ldo || m > kMaxDim / k || n > kMaxDim / k)
+    return NVFP4_ERR_INVALID_VALUE;
+  if (out_dtype != NVFP4_DTYPE_F32 && out_dtype != NVFP4_DTYPE_BF16)
+    return NVFP4_ERR_UNSUPPORTED;
+  if (epilogue != W4A4_EPI_NONE && epilogue != W4A4_EPI_ALPHA &&
+      epilogue != W4A4_EPI_BETA)
+    return NVFP4_ERR_UNSUPPORTED;
+  const int64_t os = out_dtype == NVFP4_DTYPE_F32 ? 4 : 2;
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(out, 4) ||
+      !aligned(a_global, 4) || !aligned(b_global, 4))
+    return NVFP4_ERR_MISALIGNED;
+  const int64_t obytes = ((m - 1) * ldo + n) * os;
+  if (overlap(out, obytes, a_codes, m * (k / 2)) ||
+      overlap(out, obytes, a_scales, m * (k / 16)) ||
+      overlap(out, obytes, b_codes, n * (k / 2)) ||
+      overlap(out, obytes, b_scales, n * (k / 16)) ||
+      overlap(out, obytes, a_global, 4) || overlap(out, obytes, b_global, 4))
+    return NVFP4_ERR_INVALID_VALUE;
+  return status_of(nvfp4::launch_gemm(a_codes, a_scales, a_global, m, b_codes,
+                                      b_scales, b_global, n, k, out, out_dtype,
+                                      ldo, epilogue,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

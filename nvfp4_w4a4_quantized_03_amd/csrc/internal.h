@@ -1,0 +1,32 @@
+// Internal declarations shared by the C-ABI front end (api.cpp) and the HIP
+// kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace nvfp4 {
+
+// Quantisation (quantize.hip).  Arguments are already validated.
+hipError_t launch_quantize(const void* x, int x_dtype, int64_t rows,
+                           int64_t k, int64_t ldx, uint8_t* codes,
+                           uint8_t* scales, float* global, int mode,
+                           hipStream_t stream);
+
+// Fused-group scale harmonisation (harmonize.hip).
+constexpr int kMaxModules = 64;
+hipError_t launch_harmonize(uint8_t* scales, int64_t k,
+                            const int64_t* row_offsets, int n_modules,
+                            const float* module_globals,
+                            float* shared_global, hipStream_t stream);
+
+// W4A4 GEMM (gemm.hip).
+hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
+                       const float* a_global, int64_t m,
+                       const uint8_t* b_codes, const uint8_t* b_scales,
+                       const float* b_global, int64_t n, int64_t k,
+                       void* out, int out_dtype, int64_t ldo, int epilogue,
+                       hipStream_t stream);
+
+}  // namespace nvfp4

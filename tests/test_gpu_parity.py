@@ -1,0 +1,468 @@
+"""Parity of the HIP library (through its C ABI) with the CPU oracle.
+
+Bars: NVFP4 codes, scales and globals bit-exact; GEMM fp32 output within
+relative Frobenius error 1e-5 of the exact oracle; bf16 output within one
+bf16 ulp of the oracle rounded to bf16; gates within 1e-5 relative
+Frobenius.  Small cases are compared element by element in full; the
+full-size workloads run in the launch configuration the benchmark uses and
+are checked on sampled rows/columns that the oracle computes one by one.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_w4a4_quantized_03_amd as nv
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = 1e-5
+
+
+def _say(*a):
+    print("[gpu-parity]", *a, flush=True)
+
+
+def up(vals, bits, dtype):
+    """Host tensor -> device tensor with identical bits."""
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(vals)).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)) \
+        .to(DEV).view(torch.bfloat16)
+
+
+def bf16_dev(vals):
+    bits = synth.bf16_bits_from_f32(vals)
+    return synth.f32_from_bf16_bits(bits), up(None, bits, "bf16")
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+@functools.lru_cache(maxsize=None)
+def workload(w, name):
+    vals, bits, dt = synth.workload_tensor(w, name)
+    return vals, bits, dt
+
+
+def check_quant(x_vals, q, g=None, rows=None):
+    """Compare a device NVFP4 result with the oracle (optionally on sampled
+    rows; then the global is checked against the oracle's full-tensor g)."""
+    if g is None:
+        g_ref = oracle.global_scale(x_vals)
+    else:
+        g_ref = np.float32(g)
+    g_dev = np.float32(host(q.global_scale)[0])
+    assert g_dev.view(np.uint32) == g_ref.view(np.uint32), (g_dev, g_ref)
+    sel = slice(None) if rows is None else rows
+    c_ref, s_ref, _ = oracle.quantize(x_vals[sel], g=g_ref)
+    c_dev = host(q.codes)[sel]
+    s_dev = host(q.scales)[sel]
+    bad_s = np.nonzero(s_dev != s_ref)
+    assert bad_s[0].size == 0, ("scales differ", bad_s[0][:5], bad_s[1][:5])
+    bad_c = np.nonzero(c_dev != c_ref)
+    assert bad_c[0].size == 0, ("codes differ", bad_c[0][:5], bad_c[1][:5],
+                                c_dev[bad_c][:5], c_ref[bad_c][:5])
+
+
+def sample_rows(n, count, seed):
+    rng = np.random.default_rng(seed)
+    r = set(rng.choice(n, size=min(count, n), replace=False).tolist())
+    r |= {0, n - 1, min(255, n - 1), min(256, n - 1)}
+    return np.array(sorted(r))
+
+
+def rel_frob(a, b):
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def check_bf16_within_one_ulp(y_dev_bf16, y_ref):
+    ref16, _ = oracle.bf16_rne_from_f64(y_ref)
+    got = host(y_dev_bf16.float()).astype(np.float64)
+    mag = np.maximum(np.abs(ref16), np.abs(got))
+    _, e = np.frexp(np.where(mag > 0, mag, 1.0))
+    ulp = np.ldexp(1.0, np.maximum(e - 8, -133))
+    assert np.all(np.abs(got - ref16) <= ulp)
+
+
+# ------------------------------------------------------------- quantize
+
+def test_quantize_tiny_fp32_compute():
+    for name in ("x", "w"):
+        vals, bits, dt = workload(1, name)
+        _say("quantize tiny", name, vals.shape)
+        q = nv.quantize(up(vals, bits, dt))
+        check_quant(vals, q)
+
+
+def test_quantize_worked_blocks_golden(golden):
+    for line in golden("worked_blocks.txt"):
+        head, xs, sc, packed = [p.strip() for p in line.split("|")]
+        mode, g = head.split()
+        x = np.array([np.float32(float(v)) for v in xs.split()],
+                     dtype=np.float32)[None, :]
+        gt = None if mode == "compute" else torch.tensor(
+            [float(g)], dtype=torch.float32, device=DEV)
+        for dt in ("f32", "bf16"):
+            bits = synth.bf16_bits_from_f32(x)
+            if dt == "bf16" and not np.array_equal(
+                    synth.f32_from_bf16_bits(bits), x):
+                continue
+            q = nv.quantize(up(x, bits, dt), global_scale=gt)
+            assert host(q.scales)[0, 0] == int(sc, 16), (line, dt)
+            assert bytes(host(q.codes)[0]) == bytes(
+                int(b, 16) for b in packed.split()), (line, dt)
+
+
+def _adversarial(rng, rows, k):
+    """Values on and next to every E2M1 midpoint times a block scale times
+    the global, block maxima on E4M3 midpoints, zeros of both signs,
+    sub-normal and huge magnitudes."""
+    e4 = oracle.e4m3_decode_table()[:127]
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.0, 0.0])
+    g = np.float32(2.0 ** rng.integers(-12, 6))
+    x = np.zeros((rows, k), dtype=np.float32)
+    for r in range(rows):
+        for b in range(k // 16):
+            j = rng.integers(1, 126)
+            m = np.float32(6 * g * (e4[j] + e4[j + 1]) / 2)
+            m = [m, np.nextafter(m, np.float32(0)),
+                 np.nextafter(m, np.float32(np.inf)),
+                 np.float32(6 * g * e4[j])][rng.integers(0, 4)]
+            s = oracle.block_scales(np.array([m]), g)[0]
+            d = np.float32(e4[s] * g)
+            blk = d * mids[rng.integers(0, len(mids), 16)].astype(np.float32)
+            nudge = rng.integers(-1, 2, 16)
+            blk = np.where(nudge < 0, np.nextafter(blk, np.float32(0)),
+                           np.where(nudge > 0,
+                                    np.nextafter(blk, np.float32(np.inf)),
+                                    blk)).astype(np.float32)
+            blk *= np.where(rng.random(16) < 0.5, -1, 1).astype(np.float32)
+            blk[rng.integers(0, 16)] = m
+            if rng.random() < 0.05:
+                blk[:] = 0
+                blk[rng.integers(0, 16)] = -0.0
+            x[r, b * 16:(b + 1) * 16] = blk
+    return x, g
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_quantize_adversarial_ties_fp32(seed):
+    rng = np.random.default_rng(100 + seed)
+    x, g = _adversarial(rng, 64, 256)
+    _say("quantize adversarial seed", seed, "g", g)
+    xd = up(x, None, "f32")
+    check_quant(x, nv.quantize(xd, global_scale=torch.tensor(
+        [g], dtype=torch.float32, device=DEV)), g=g)
+    check_quant(x, nv.quantize(xd))
+
+
+def test_quantize_adversarial_bf16():
+    rng = np.random.default_rng(7)
+    x, g = _adversarial(rng, 64, 256)
+    xb, xd = bf16_dev(x)
+    check_quant(xb, nv.quantize(xd))
+    check_quant(xb, nv.quantize(xd, global_scale=torch.tensor(
+        [g], dtype=torch.float32, device=DEV)), g=g)
+
+
+@pytest.mark.parametrize("g", [0.0, 1e-45, 1e-40, 3e-38, 1e-30, 1e-3, 1.0,
+                               7.3e5, 1e30, 1e35])
+def test_quantize_given_global_extremes(g):
+    """Given globals across the binary32 range, including 0 and
+    subnormals, on data of several magnitudes (saturating and underflowing
+    blocks included)."""
+    rng = np.random.default_rng(int(abs(np.log10(g + 1e-50)) * 10))
+    x = (rng.standard_normal((16, 128)) *
+         np.float32(10.0) ** rng.integers(-38, 37, (16, 1))).astype(
+             np.float32)
+    x[3, 5] = -0.0
+    x[4, :16] = 0
+    x[5, 16:32] = np.float32(1e-45)
+    x[6, 32] = np.float32(3.3e38)
+    gt = torch.tensor([g], dtype=torch.float32, device=DEV)
+    _say("quantize given global", g)
+    check_quant(x, nv.quantize(up(x, None, "f32"), global_scale=gt),
+                g=np.float32(g))
+    xb, xd = bf16_dev(x)
+    check_quant(xb, nv.quantize(xd, global_scale=gt), g=np.float32(g))
+
+
+def test_quantize_degenerate_tensors():
+    zeros = np.zeros((3, 32), dtype=np.float32)
+    q = nv.quantize(up(zeros, None, "f32"))
+    check_quant(zeros, q)
+    assert host(q.global_scale)[0] == 0
+    negz = -zeros
+    check_quant(negz, nv.quantize(up(negz, None, "f32")))
+    tiny = np.full((2, 16), np.float32(1e-45), dtype=np.float32)
+    check_quant(tiny, nv.quantize(up(tiny, None, "f32")))   # g underflows
+    huge = np.full((2, 16), np.float32(3.3e38), dtype=np.float32)
+    huge[1, 3] = -1.0
+    check_quant(huge, nv.quantize(up(huge, None, "f32")))
+    one = np.zeros((1, 16), dtype=np.float32)
+    one[0, 7] = 5.0
+    check_quant(one, nv.quantize(up(one, None, "f32")))
+
+
+@pytest.mark.parametrize("rows,k,pad", [(1, 16, 0), (3, 48, 8), (257, 272, 0),
+                                        (5, 5136, 24), (130, 4096, 64)])
+def test_quantize_ragged_and_strided(rows, k, pad):
+    rng = np.random.default_rng(rows * 7 + k)
+    full = rng.standard_normal((rows, k + pad)).astype(np.float32)
+    x = full[:, :k]
+    _say("quantize ragged", rows, k, pad)
+    xd = up(full, None, "f32")[:, :k]
+    check_quant(x, nv.quantize(xd))
+    fb, fd = bf16_dev(full)
+    check_quant(fb[:, :k], nv.quantize(fd[:, :k]))
+
+
+@pytest.mark.parametrize("w,name", [(2, "x"), (2, "w"), (5, "x"),
+                                    (5, "x_dec"), (3, "w_a")])
+def test_quantize_full_size(w, name):
+    vals, bits, dt = workload(w, name)
+    _say("quantize full size", w, name, vals.shape)
+    xd = up(vals, bits, dt)
+    rows = sample_rows(vals.shape[0], 192, w)
+    check_quant(vals, nv.quantize(xd), rows=rows)
+    g = np.float32(oracle.global_scale(vals) * np.float32(1.5))
+    check_quant(vals, nv.quantize(xd, global_scale=torch.tensor(
+        [g], dtype=torch.float32, device=DEV)), g=g, rows=rows)
+
+
+# ------------------------------------------------------------ harmonize
+
+def test_harmonize_every_scale_byte():
+    allb = np.arange(0, 0x7F, dtype=np.uint8)
+    sc = np.tile(allb, (6, 1)).reshape(6, 127)
+    sc = np.concatenate([sc, np.zeros((6, 1), np.uint8)], axis=1)  # k=2048
+    for ratios in ([0.5, 1.0, 0.75], [1 / 3, 0.5625, 1.0],
+                   [1e-3, 1.0, 0.999], [0.0, 1.0, 0.3]):
+        gs = [np.float32(r) for r in ratios]
+        offs = [0, 2, 4, 6]
+        ref, gstar = oracle.harmonize(sc, offs, gs)
+        d = torch.from_numpy(sc.copy()).to(DEV)
+        gd = torch.tensor(gs, dtype=torch.float32, device=DEV)
+        out = nv.harmonize_group(d, 2048, offs, gd)
+        assert host(out)[0] == gstar
+        assert np.array_equal(host(d), ref), ratios
+
+
+def test_harmonize_fused_group_full_size():
+    """Three modules with different per-module globals quantised into row
+    slices of one fused buffer, then harmonised (the fused qkv|z style
+    group of the pages)."""
+    mods = ["w1", "w2", "w3"]
+    sizes = [synth.workload_shape(4, m)[0] for m in mods]
+    k = 5120
+    offs = [0] + list(np.cumsum(sizes))
+    n_tot = offs[-1]
+    codes = torch.empty((n_tot, k // 2), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((n_tot, k // 16), dtype=torch.uint8, device=DEV)
+    gdev = torch.empty(3, dtype=torch.float32, device=DEV)
+    ref_scales, ref_g = [], []
+    for i, mname in enumerate(mods):
+        vals, bits, dt = workload(4, mname)
+        q = nv.quantize(up(vals, bits, dt), out=(codes[offs[i]:offs[i + 1]],
+                                                 scales[offs[i]:offs[i + 1]]))
+        gdev[i:i + 1].copy_(q.global_scale)
+        rows = sample_rows(sizes[i], 64, i)
+        check_quant(vals, q, rows=rows)
+        ref_g.append(oracle.global_scale(vals))
+        _, s_ref, _ = oracle.quantize(vals[rows], g=ref_g[-1])
+        ref_scales.append((rows + offs[i], s_ref))
+    gstar = nv.harmonize_group(scales, k, offs, gdev)
+    all_rows = np.concatenate([r for r, _ in ref_scales])
+    all_s = np.concatenate([s for _, s in ref_scales])
+    # the oracle's harmonisation of the same sampled rows
+    sub_offs = [0] + list(np.cumsum([len(r) for r, _ in ref_scales]))
+    want, g_ref = oracle.harmonize(all_s, sub_offs, ref_g)
+    assert host(gstar)[0] == g_ref
+    assert np.array_equal(host(scales)[all_rows], want)
+    assert len(set(float(g) for g in ref_g)) == 3
+
+
+# ------------------------------------------------------------------ gemm
+
+def _quant_pair(xv, xd, wv, wd):
+    qa, qb = nv.quantize(xd), nv.quantize(wd)
+    return qa, qb
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_gemm_tiny_exact(out_dtype):
+    xv, xb, xt = workload(1, "x")
+    wv, wb, wt = workload(1, "w")
+    qa = nv.quantize(up(xv, xb, xt))
+    qb = nv.quantize(up(wv, wb, wt))
+    check_quant(xv, qa)
+    check_quant(wv, qb)
+    ref = oracle.gemm_exact_int(*oracle.quantize(xv), *oracle.quantize(wv))
+    y = nv.gemm(qa, qb, out_dtype=out_dtype)
+    if out_dtype == torch.float32:
+        assert rel_frob(host(y).astype(np.float64), ref) <= TOL
+    else:
+        check_bf16_within_one_ulp(y, ref)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1, 16), (33, 65, 48), (300, 130, 272),
+                                   (17, 300, 5136), (257, 513, 1024),
+                                   (64, 64, 4096)])
+def test_gemm_ragged_shapes(m, n, k):
+    rng = np.random.default_rng(m * 31 + n * 7 + k)
+    xv = rng.standard_normal((m, k)).astype(np.float32)
+    wv = (rng.standard_normal((n, k)) * 0.05).astype(np.float32)
+    _say("gemm ragged", m, n, k)
+    qa = nv.quantize(up(xv, None, "f32"))
+    qb = nv.quantize(up(wv, None, "f32"))
+    ref = oracle.gemm_exact_int(*oracle.quantize(xv), *oracle.quantize(wv))
+    y = host(nv.gemm(qa, qb, out_dtype=torch.float32)).astype(np.float64)
+    assert rel_frob(y, ref) <= TOL
+    check_bf16_within_one_ulp(nv.gemm(qa, qb, out_dtype=torch.bfloat16), ref)
+    ya = host(nv.gemm(qa, qb, out_dtype=torch.float32, epilogue="alpha"))
+    assert rel_frob(ya.astype(np.float64), oracle.gate_alpha(ref)) <= TOL
+    yb = host(nv.gemm(qa, qb, out_dtype=torch.float32, epilogue="beta"))
+    assert rel_frob(yb.astype(np.float64), oracle.gate_beta(ref)) <= TOL
+
+
+def test_gemm_strided_output():
+    rng = np.random.default_rng(3)
+    xv = rng.standard_normal((40, 256)).astype(np.float32)
+    wv = rng.standard_normal((24, 256)).astype(np.float32)
+    qa = nv.quantize(up(xv, None, "f32"))
+    qb = nv.quantize(up(wv, None, "f32"))
+    big = torch.full((40, 64), 7.0, dtype=torch.float32, device=DEV)
+    nv.gemm(qa, qb, out_dtype=torch.float32, out=big[:, 8:32])
+    ref = oracle.gemm_exact_int(*oracle.quantize(xv), *oracle.quantize(wv))
+    got = host(big)
+    assert rel_frob(got[:, 8:32].astype(np.float64), ref) <= TOL
+    assert np.all(got[:, :8] == 7.0) and np.all(got[:, 32:] == 7.0)
+
+
+def _sampled_gemm_check(xv, qa, wv, qb, rows, cols, y_dev, out_dtype,
+                        epilogue="none"):
+    ca, sa, ga = oracle.quantize(xv[rows], g=oracle.global_scale(xv))
+    cb, sb, gb = oracle.quantize(wv[cols], g=oracle.global_scale(wv))
+    ref = oracle.gemm_f64(ca, sa, ga, cb, sb, gb)
+    if epilogue == "alpha":
+        ref = oracle.gate_alpha(ref)
+    elif epilogue == "beta":
+        ref = oracle.gate_beta(ref)
+    got = y_dev[torch.from_numpy(rows).to(DEV)][:, torch.from_numpy(cols)
+                                                 .to(DEV)]
+    if out_dtype == torch.float32:
+        err = rel_frob(host(got).astype(np.float64), ref)
+        _say("sampled rel-Frob", err)
+        assert err <= TOL
+    else:
+        check_bf16_within_one_ulp(got, ref)
+
+
+def test_gemm_gdn_in_proj_full_size():
+    xv, xb, xt = workload(2, "x")
+    wv, wb, wt = workload(2, "w")
+    _say("gemm in_proj 4096x12288x5120")
+    qa = nv.quantize(up(xv, xb, xt))
+    qb = nv.quantize(up(wv, wb, wt))
+    rows = sample_rows(4096, 96, 21)
+    cols = sample_rows(12288, 96, 22)
+    for od in (torch.bfloat16, torch.float32):
+        y = nv.gemm(qa, qb, out_dtype=od)
+        _sampled_gemm_check(xv, qa, wv, qb, rows, cols, y, od)
+
+
+def test_gemm_gate_projections_full_size():
+    xv, xb, xt = workload(3, "x")
+    _say("gemm gates 32768x64x5120")
+    qa = nv.quantize(up(xv, xb, xt))
+    rows = sample_rows(32768, 256, 31)
+    cols = np.arange(64)
+    for name, epi in (("w_a", "alpha"), ("w_b", "beta")):
+        wv, wb, wt = workload(3, name)
+        qb = nv.quantize(up(wv, wb, wt))
+        y = nv.gemm(qa, qb, out_dtype=torch.float32, epilogue=epi)
+        _sampled_gemm_check(xv, qa, wv, qb, rows, cols, y, torch.float32, epi)
+        y = nv.gemm(qa, qb, out_dtype=torch.float32)
+        _sampled_gemm_check(xv, qa, wv, qb, rows, cols, y, torch.float32)
+
+
+def test_gemm_fused_group_after_harmonize():
+    mods = ["w1", "w2", "w3"]
+    sizes = [synth.workload_shape(4, m)[0] for m in mods]
+    k = 5120
+    offs = [0] + list(np.cumsum(sizes))
+    codes = torch.empty((offs[-1], k // 2), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((offs[-1], k // 16), dtype=torch.uint8, device=DEV)
+    gdev = torch.empty(3, dtype=torch.float32, device=DEV)
+    wvals = []
+    for i, mname in enumerate(mods):
+        vals, bits, dt = workload(4, mname)
+        wvals.append(vals)
+        q = nv.quantize(up(vals, bits, dt), out=(codes[offs[i]:offs[i + 1]],
+                                                 scales[offs[i]:offs[i + 1]]))
+        gdev[i:i + 1].copy_(q.global_scale)
+    gstar = nv.harmonize_group(scales, k, offs, gdev)
+    xv, xb, xt = workload(4, "x")
+    qa = nv.quantize(up(xv, xb, xt))
+    y = nv.gemm(qa, nv.NVFP4(codes, scales, gstar), out_dtype=torch.float32)
+    # oracle: quantise each module with its own global, harmonise, GEMM
+    rows = sample_rows(8192, 64, 41)
+    cols_per = [sample_rows(s, 40, 42 + i) for i, s in enumerate(sizes)]
+    ca, sa, ga = oracle.quantize(xv[rows], g=oracle.global_scale(xv))
+    gs = [oracle.global_scale(v) for v in wvals]
+    parts = [oracle.quantize(v[c], g=g) for v, c, g in zip(wvals, cols_per,
+                                                           gs)]
+    bc = np.concatenate([p[0] for p in parts])
+    bs = np.concatenate([p[1] for p in parts])
+    sub_offs = [0] + list(np.cumsum([len(c) for c in cols_per]))
+    bs_h, g_ref = oracle.harmonize(bs, sub_offs, gs)
+    ref = oracle.gemm_f64(ca, sa, ga, bc, bs_h, g_ref)
+    cols = np.concatenate([c + offs[i] for i, c in enumerate(cols_per)])
+    got = host(y[torch.from_numpy(rows).to(DEV)][:, torch.from_numpy(cols)
+                                                 .to(DEV)])
+    assert rel_frob(got.astype(np.float64), ref) <= TOL
+
+
+def test_gemm_prefill_and_decode_full_size():
+    xv, xb, xt = workload(5, "x")
+    dv, db, dt_ = workload(5, "x_dec")
+    wv, wb, wt = workload(5, "w")
+    _say("gemm prefill 32768x10240x5120 + decode 32")
+    qb = nv.quantize(up(wv, wb, wt))
+    qa = nv.quantize(up(xv, xb, xt))
+    rows = sample_rows(32768, 64, 51)
+    cols = sample_rows(10240, 64, 52)
+    y = nv.gemm(qa, qb, out_dtype=torch.bfloat16)
+    _sampled_gemm_check(xv, qa, wv, qb, rows, cols, y, torch.bfloat16)
+    del y
+    y = nv.gemm(qa, qb, out_dtype=torch.float32)
+    _sampled_gemm_check(xv, qa, wv, qb, rows, cols, y, torch.float32)
+    del y
+    qd = nv.quantize(up(dv, db, dt_))
+    check_quant(dv, qd)
+    yd = nv.gemm(qd, qb, out_dtype=torch.float32)
+    cols = sample_rows(10240, 512, 53)
+    _sampled_gemm_check(dv, qd, wv, qb, np.arange(32), cols, yd,
+                        torch.float32)
+    ydb = nv.gemm(qd, qb, out_dtype=torch.bfloat16)
+    _sampled_gemm_check(dv, qd, wv, qb, np.arange(32), cols, ydb,
+                        torch.bfloat16)
+
+
+def test_calls_on_a_side_stream():
+    rng = np.random.default_rng(8)
+    xv = rng.standard_normal((64, 512)).astype(np.float32)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        xd = up(xv, None, "f32")
+        q = nv.quantize(xd)
+        y = nv.gemm(q, q, out_dtype=torch.float32)
+    s.synchronize()
+    check_quant(xv, q)
+    ref = oracle.gemm_exact_int(*oracle.quantize(xv), *oracle.quantize(xv))
+    assert rel_frob(host(y).astype(np.float64), ref) <= TOL
