@@ -1,0 +1,263 @@
+"""Benchmark of the NVFP4 W4A4 hot path on one MI355X.
+
+One step = the long-prefill + decode workload at hidden size 5120:
+  quantize X[32768 x 5120] bf16 to NVFP4 with a calibrated (given) global,
+  W4A4 GEMM against the pre-quantized weight W[10240 x 5120] -> bf16,
+  quantize X[32 x 5120] (decode batch), W4A4 GEMM -> bf16.
+Inputs are seeded synthetic tensors (synth.py) already resident in HBM when
+the timed region starts; the weight is quantised once before timing.
+
+Prints one JSON line: whole-step throughput (TFLOP/s over 2 K N (M + M_dec)
+flops), per-kernel HIP-event timings on the launch stream, the GEMM's
+roofline fraction against the dense fp16/bf16 MFMA peak, the quantiser's
+against HBM, and the CPU oracle timed on a bounded sample of the same work.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("W4A4 GEMM TFLOP/s + NVFP4 quantize GB/s at K=5120, "
+          "as % of MI355X peak")
+PEAK_MFMA_TFLOPS = 2500.0        # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBPS = 8000.0           # MI355X HBM3E
+M, M_DEC, N, K = 32768, 32, 10240, 5120
+WORKLOAD = 5
+KERNEL_SOURCES = ["gemm.hip", "quantize.hip"]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def source_hash(name):
+    path = os.path.join(ROOT, "nvfp4_w4a4_quantized_03_amd", "csrc", name)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel_file, per_launch_units):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", kernel_file)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    src = re.search(r"source_sha256_16:\s*(\w+)", text)
+    byt = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    kern = re.search(r"kernel_source:\s*(\S+)", text)
+    if not (src and byt and kern) or src.group(1) != source_hash(kern.group(1)):
+        return None
+    return float(byt.group(1))
+
+
+def cpu_baseline():
+    """The oracle, as it stands, on a bounded sample of the step's work:
+    quantize 8192 rows of X (numpy, one core) and the W4A4 GEMM of 2048 of
+    those rows against 4096 weight rows (float64 BLAS on the decoded
+    operands, all BLAS threads).  Scaled to the whole step's flops."""
+    import oracle
+    import synth
+    from threadpoolctl import threadpool_info
+    GM, GN = 2048, 4096
+    xv, _, _ = synth.workload_tensor(WORKLOAD, "x", row_ids=np.arange(8192))
+    wv, _, _ = synth.workload_tensor(WORKLOAD, "w", row_ids=np.arange(GN))
+    g = np.float32(0.25)
+    t0 = time.perf_counter()
+    qa = oracle.quantize(xv, g=g)
+    tq = time.perf_counter() - t0
+    qb = oracle.quantize(wv, g=g)
+    qa = tuple(t[:GM] if t.ndim else t for t in qa)
+    t0 = time.perf_counter()
+    oracle.gemm_f64(*qa, *qb)
+    tg = time.perf_counter() - t0
+    # per-element quantize time and per-flop GEMM time, scaled to one step
+    q_elems = (M + M_DEC) * K
+    t_step = tq / xv.size * q_elems + tg / (2.0 * GM * GN * K) * \
+        (2.0 * (M + M_DEC) * N * K)
+    blas = max([d.get("num_threads", 1) for d in threadpool_info()
+                if d.get("user_api") == "blas"] or [1])
+    return {
+        "value": 2.0 * (M + M_DEC) * N * K / t_step / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(blas),
+        "kind": "oracle",
+        "sample": ("oracle.quantize of X rows 0..8191 (%.2f s, 1 core) and "
+                   "oracle.gemm_f64 2048x4096x5120 (%.2f s, %d BLAS threads), "
+                   "scaled per element / per flop to one step "
+                   "(quantize 32800x5120 + GEMM 32800x10240x5120)"
+                   % (tq, tg, blas)),
+        "quantize_gbps": xv.size * 2.5625 / tq / 1e9,
+        "gemm_tflops": 2.0 * GM * GN * K / tg / 1e12,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the NVFP4 W4A4 path here is "
+              "single-GPU (no collectives); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import nvfp4_w4a4_quantized_03_amd as nv
+    import oracle
+    import synth
+
+    dev = torch.device("cuda:0")
+    print("[bench] generating synthetic inputs", file=sys.stderr, flush=True)
+    xv, xbits, _ = synth.workload_tensor(WORKLOAD, "x")
+    dv, dbits, _ = synth.workload_tensor(WORKLOAD, "x_dec")
+    wv, wbits, _ = synth.workload_tensor(WORKLOAD, "w")
+
+    def upload(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(
+            torch.bfloat16)
+
+    x, xd, w = upload(xbits), upload(dbits), upload(wbits)
+    del xbits, dbits, wbits
+    stream = torch.cuda.current_stream(dev)
+
+    # weights are pre-quantised (offline); activation globals are the
+    # calibrated static values (here: the tensors' own amax-derived g)
+    qw = nv.quantize(w)
+    gx = nv.quantize(x).global_scale.clone()
+    gd = nv.quantize(xd).global_scale.clone()
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    yd = torch.empty((M_DEC, N), dtype=torch.bfloat16, device=dev)
+    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+    dcodes = torch.empty((M_DEC, K // 2), dtype=torch.uint8, device=dev)
+    dscales = torch.empty((M_DEC, K // 16), dtype=torch.uint8, device=dev)
+
+    names = ["quantize", "gemm", "quantize_dec", "gemm_dec"]
+    ev = {n: [] for n in names}
+
+    def step(record):
+        marks = []
+        if record:
+            marks.append(torch.cuda.Event(enable_timing=True))
+            marks[-1].record(stream)
+        qa = nv.quantize(x, global_scale=gx, out=(codes, scales))
+        if record:
+            marks.append(torch.cuda.Event(enable_timing=True))
+            marks[-1].record(stream)
+        nv.gemm(qa, qw, out_dtype=torch.bfloat16, out=y)
+        if record:
+            marks.append(torch.cuda.Event(enable_timing=True))
+            marks[-1].record(stream)
+        qd = nv.quantize(xd, global_scale=gd, out=(dcodes, dscales))
+        if record:
+            marks.append(torch.cuda.Event(enable_timing=True))
+            marks[-1].record(stream)
+        nv.gemm(qd, qw, out_dtype=torch.bfloat16, out=yd)
+        if record:
+            marks.append(torch.cuda.Event(enable_timing=True))
+            marks[-1].record(stream)
+            for i, nme in enumerate(names):
+                ev[nme].append((marks[i], marks[i + 1]))
+
+    print("[bench] warmup", args.warmup, file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+
+    # the timed region: exactly K steps, synchronised on both sides
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    print("[bench] timed %d steps in %.3f s" % (args.steps, elapsed),
+          file=sys.stderr, flush=True)
+
+    avg_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]]))
+              for n in names}
+    flops_gemm = 2.0 * M * N * K
+    flops_step = 2.0 * (M + M_DEC) * N * K
+    ms_step = elapsed * 1e3 / args.steps
+    q_bytes = M * K * 2.5625           # bf16 in, codes + scales out
+    gemm_tflops = flops_gemm / (avg_ms["gemm"] * 1e-3) / 1e12
+    q_gbps = q_bytes / (avg_ms["quantize"] * 1e-3) / 1e9
+    dec_bytes = N * K * 0.5625 + M_DEC * K * 0.5625 + M_DEC * N * 2
+    # sampled parity of this very run's outputs against the oracle
+    rows = np.array([0, 1, 4095, 16384, M - 1])
+    cols = np.array([0, 7, 5000, N - 1])
+    g_x = np.float32(gx.cpu().numpy()[0])
+    ca, sa, _ = oracle.quantize(xv[rows], g=g_x)
+    cb, sb, gb = oracle.quantize(wv[cols], g=oracle.global_scale(wv))
+    ref = oracle.gemm_f64(ca, sa, g_x, cb, sb, gb)
+    got = y[torch.from_numpy(rows).to(dev)][:, torch.from_numpy(cols).to(
+        dev)].float().cpu().numpy().astype(np.float64)
+    ref16, _ = oracle.bf16_rne_from_f64(ref)
+    parity_ok = bool(np.all(np.abs(got - ref16) <= np.abs(ref16) * 2.0 ** -7
+                            + 1e-30))
+
+    traffic = measured_traffic("w4a4_gemm_prefill_32768x10240x5120_traffic.md",
+                               1)
+    out = {
+        "metric": METRIC,
+        "value": flops_step / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4->f16 mfma, f32 acc",
+        "data": "synthetic",
+        "config": {"workload": "long prefill + decode, hidden 5120: "
+                               "X[32768x5120] and X[32x5120] bf16 (1% outlier "
+                               "channels x60), W[10240x5120] bf16 N(0,0.02) "
+                               "pre-quantized; NVFP4 activation quantize per "
+                               "call (given global) + W4A4 GEMM, bf16 out",
+                   "M": M, "M_decode": M_DEC, "N": N, "K": K},
+        "roofline": {"bound": "mfma", "achieved": gemm_tflops,
+                     "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": gemm_tflops / PEAK_MFMA_TFLOPS,
+                     "traffic": traffic},
+        "kernels": {
+            "gemm_prefill": {"us": avg_ms["gemm"] * 1e3,
+                             "tflops": gemm_tflops,
+                             "frac_mfma_peak": gemm_tflops / PEAK_MFMA_TFLOPS},
+            "quantize_prefill": {"us": avg_ms["quantize"] * 1e3,
+                                 "gbps": q_gbps,
+                                 "frac_hbm_peak": q_gbps / PEAK_HBM_GBPS,
+                                 "bytes": q_bytes},
+            "quantize_decode": {"us": avg_ms["quantize_dec"] * 1e3},
+            "gemm_decode": {"us": avg_ms["gemm_dec"] * 1e3,
+                            "gbps": dec_bytes / (avg_ms["gemm_dec"] * 1e-3)
+                            / 1e9,
+                            "frac_hbm_peak": dec_bytes /
+                            (avg_ms["gemm_dec"] * 1e-3) / 1e9 /
+                            PEAK_HBM_GBPS},
+        },
+        "parity_sample_ok": parity_ok,
+        "kernel_sources_sha256_16": {s: source_hash(s)
+                                     for s in KERNEL_SOURCES},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr,
+              flush=True)
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
