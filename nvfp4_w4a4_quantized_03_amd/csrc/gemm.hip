@@ -49,15 +49,6 @@ constexpr int kCodeBytes = kBK / 2;      // 64 code bytes per row per stage
 constexpr int kCodeStride = kCodeBytes + 16;  // padded LDS row (bytes)
 constexpr int kScalesPerRow = kBK / 16;  // 8 block scales per row per stage
 
-// OCP E4M3 byte (0x00..0x7E) -> fp16 bits, exact.  Normal codes map by a
-// shift and an exponent rebias (7 -> 15); subnormals m * 2^-9 go through
-// binary32.
-__device__ __forceinline__ unsigned short e4m3_to_f16_bits(unsigned c) {
-  if (c >= 8u) return static_cast<unsigned short>((c << 7) + 0x2000u);
-  const _Float16 h = static_cast<_Float16>(static_cast<float>(c) * 0.001953125f);
-  return __builtin_bit_cast(unsigned short, h);
-}
-
 // Decode 8 codes (one dword, element 2j in the low nibble of byte j) with
 // one fp16 block scale into 8 exact fp16 values.
 __device__ __forceinline__ half8_t decode8(unsigned codes, half2_t sc) {
@@ -91,32 +82,46 @@ __device__ __forceinline__ float epilogue(float y) {
 }
 
 // Copies one operand's BK-wide stage (ROWS rows of codes and scales) from
-// global memory to LDS.  Rows past `rows` and K past `k` read as zero.
+// global memory to LDS through registers.
+//
+// ALIGNED (k % 128 == 0, the shapes of the workloads): every 16-byte code
+// chunk and every row's 8 scale bytes of a stage lie inside k, so loads are
+// unconditional (rows past `rows` read a clamped, valid row) and row validity
+// is applied when storing to LDS.  No load result is consumed before the
+// store, so all of a stage's loads are in flight together.  Scales are
+// widened to fp16 by the gfx950 fp8 conversion (OCP E4M3, exact in fp16).
+//
+// Otherwise (ragged k) each 8-byte half-chunk and each scale byte is
+// guarded individually.
 template <int ROWS, int NT, bool ALIGNED>
 struct StageLoader {
   static constexpr int kChunks = ROWS * (kCodeBytes / 16);   // 16-byte chunks
   static constexpr int kPerThread = (kChunks + NT - 1) / NT;
-  static constexpr int kScalePerThread = (ROWS * kScalesPerRow + NT - 1) / NT;
+  static constexpr int kScaleRows = (ROWS + NT - 1) / NT;     // rows per thread
   uint4 code[kPerThread];
-  unsigned char sc[kScalePerThread];
+  uint2 sc[kScaleRows];
+  unsigned valid;   // bit i: chunk i is inside the matrix; bit 16+j: scale row j
 
   __device__ __forceinline__ void load(const uint8_t* __restrict__ codes,
                                        const uint8_t* __restrict__ scales,
                                        int64_t row0, int64_t rows, int64_t k,
                                        int64_t k0, int tid) {
     const int64_t kbytes = k / 2, kblocks = k / 16;
+    valid = 0u;
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
       const int c = tid + i * NT;
       const int r = c / (kCodeBytes / 16), part = c % (kCodeBytes / 16);
       const int64_t grow = row0 + r;
       const int64_t kb = k0 / 2 + part * 16;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (c < kChunks && grow < rows) {
-        const uint8_t* p = codes + grow * kbytes + kb;
-        if (ALIGNED && kb + 16 <= kbytes) {
-          v = *reinterpret_cast<const uint4*>(p);
-        } else {
+      if constexpr (ALIGNED) {
+        const int64_t srow = grow < rows ? grow : rows - 1;
+        code[i] = *reinterpret_cast<const uint4*>(codes + srow * kbytes + kb);
+        valid |= (c < kChunks && grow < rows) ? (1u << i) : 0u;
+      } else {
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (c < kChunks && grow < rows) {
+          const uint8_t* p = codes + grow * kbytes + kb;
           if (kb + 8 <= kbytes) {
             const uint2 lo = *reinterpret_cast<const uint2*>(p);
             v.x = lo.x; v.y = lo.y;
@@ -126,19 +131,30 @@ struct StageLoader {
             v.z = hi.x; v.w = hi.y;
           }
         }
+        code[i] = v;
+        valid |= 1u << i;
       }
-      code[i] = v;
     }
 #pragma unroll
-    for (int i = 0; i < kScalePerThread; ++i) {
-      const int c = tid + i * NT;
-      const int r = c / kScalesPerRow, j = c % kScalesPerRow;
+    for (int j = 0; j < kScaleRows; ++j) {
+      const int r = tid + j * NT;
       const int64_t grow = row0 + r;
-      const int64_t blk = k0 / 16 + j;
-      unsigned char v = 0;
-      if (c < ROWS * kScalesPerRow && grow < rows && blk < kblocks)
-        v = scales[grow * kblocks + blk];
-      sc[i] = v;
+      const int64_t blk = k0 / 16;
+      if constexpr (ALIGNED) {
+        const int64_t srow = grow < rows ? grow : rows - 1;
+        sc[j] = *reinterpret_cast<const uint2*>(scales + srow * kblocks + blk);
+        valid |= (r < ROWS && grow < rows) ? (1u << (16 + j)) : 0u;
+      } else {
+        unsigned w[2] = {0u, 0u};
+        if (r < ROWS && grow < rows) {
+#pragma unroll
+          for (int b = 0; b < kScalesPerRow; ++b)
+            if (blk + b < kblocks)
+              w[b >> 2] |= static_cast<unsigned>(scales[grow * kblocks + blk + b]) << (8 * (b & 3));
+        }
+        sc[j] = make_uint2(w[0], w[1]);
+        valid |= 1u << (16 + j);
+      }
     }
   }
 
@@ -150,13 +166,28 @@ struct StageLoader {
       const int c = tid + i * NT;
       if (c < kChunks) {
         const int r = c / (kCodeBytes / 16), part = c % (kCodeBytes / 16);
-        *reinterpret_cast<uint4*>(lds_codes + r * kCodeStride + part * 16) = code[i];
+        const uint4 v = (valid >> i) & 1u ? code[i] : make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(lds_codes + r * kCodeStride + part * 16) = v;
       }
     }
 #pragma unroll
-    for (int i = 0; i < kScalePerThread; ++i) {
-      const int c = tid + i * NT;
-      if (c < ROWS * kScalesPerRow) lds_scales[c] = e4m3_to_f16_bits(sc[i]);
+    for (int j = 0; j < kScaleRows; ++j) {
+      const int r = tid + j * NT;
+      if (r < ROWS) {
+        const bool ok = (valid >> (16 + j)) & 1u;
+        const unsigned lo = ok ? sc[j].x : 0u, hi = ok ? sc[j].y : 0u;
+        // four gfx950 conversions: 8 E4M3 bytes -> 8 fp16 (exact)
+        const half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+        const half2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+        const half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+        const half2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+        uint4 out;
+        out.x = __builtin_bit_cast(unsigned, h0);
+        out.y = __builtin_bit_cast(unsigned, h1);
+        out.z = __builtin_bit_cast(unsigned, h2);
+        out.w = __builtin_bit_cast(unsigned, h3);
+        *reinterpret_cast<uint4*>(lds_scales + r * kScalesPerRow) = out;
+      }
     }
   }
 };
@@ -304,6 +335,388 @@ w4a4_gemm_kernel(const uint8_t* __restrict__ a_codes,
     }
 }
 
+#ifndef PIPE_STAGES
+#define PIPE_STAGES 4
+#endif
+#ifndef PIPE_DS_HINT
+#define PIPE_DS_HINT __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+#endif
+
+// ---------------------------------------------------------------------------
+// Pipelined kernel for large, whole-stage shapes (k % 128 == 0).
+//
+// * Operand stages go from global memory straight into LDS (gfx950
+//   global_load_lds_dwordx4 / _dword: no staging registers, no LDS store
+//   instructions).  Codes are stored unpadded, 64 bytes per row per stage,
+//   with the four 16-byte chunks of row r permuted by XOR with (r / 4) % 4 so
+//   that 16 lanes reading 16 consecutive rows hit 16 distinct bank groups.
+//   Scales stay raw E4M3 (8 bytes per row per stage) and are widened to
+//   fp16 when a fragment is read.
+// * Three LDS stages form a ring: stage kt + 2 is fetched while stage kt is
+//   consumed, and stage kt + 1 is already resident, so the next half-stage's
+//   fragments are read one half ahead and the next k-step's operands are
+//   decoded while the 16 MFMAs of the current k-step issue.  One wait for the
+//   stage's own loads and one barrier per stage keep the ring ordered: stage
+//   kt + 2 goes into the slot of stage kt - 1, which every wave finished
+//   before the barrier that closed stage kt - 1.
+// * Rows past m or n load a clamped (valid) row; their outputs are never
+//   stored.
+
+constexpr int kPipeRowBytes = kCodeBytes;        // 64, unpadded
+constexpr int kPipeScaleBytes = kScalesPerRow;   // 8 raw E4M3 bytes
+
+__device__ __forceinline__ int pipe_chunk(int row, int part) {
+  return row * 4 + (part ^ ((row >> 2) & 3));
+}
+
+// A wave's fragments for one half-stage (4 k-steps, 64 K per lane half):
+// per 32-row tile, 16 code bytes and the two fp16 scales of its blocks.
+template <int T>
+struct HalfFrags {
+  uint4 code[T];
+  unsigned scale[T];
+
+  __device__ __forceinline__ void read(const uint8_t* lds_codes,
+                                       const uint8_t* lds_scales,
+                                       int row_base, int lane, int half) {
+    const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int row = row_base + t * 32 + r;
+      code[t] = *reinterpret_cast<const uint4*>(lds_codes + pipe_chunk(row, 2 * h + half) * 16);
+      const unsigned raw = *reinterpret_cast<const unsigned*>(lds_scales + row * kPipeScaleBytes + 4 * h);
+      scale[t] = half ? __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw, 1.0f, true))
+                      : __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw, 1.0f, false));
+    }
+  }
+
+  // operand of k-step j (0..3) of this half: 8 codes, block j / 2.
+  __device__ __forceinline__ half8_t operand(int t, int j) const {
+    const uint4 q = code[t];
+    const unsigned w = j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
+    const unsigned short sb = (j >> 1) ? static_cast<unsigned short>(scale[t] >> 16)
+                                       : static_cast<unsigned short>(scale[t] & 0xFFFFu);
+    const _Float16 sv = __builtin_bit_cast(_Float16, sb);
+    half2_t sc;
+    sc[0] = sv;
+    sc[1] = sv;
+    return decode8(w, sc);
+  }
+};
+
+template <int TM, int TN>
+struct Operands {
+  half8_t a[TM];
+  half8_t b[TN];
+};
+
+template <int TM, int TN>
+__device__ __forceinline__ void decode_step(Operands<TM, TN>& o, const HalfFrags<TM>& fa,
+                                            const HalfFrags<TN>& fb, int j) {
+#pragma unroll
+  for (int i = 0; i < TM; ++i) o.a[i] = fa.operand(i, j);
+#pragma unroll
+  for (int i = 0; i < TN; ++i) o.b[i] = fb.operand(i, j);
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void mfma_step(float16_t (&acc)[TM][TN], const Operands<TM, TN>& o) {
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(o.a[i], o.b[j], acc[i][j], 0, 0, 0);
+}
+
+// Scheduling hint for one k-step: alternate one MFMA with a few VALU ops
+// (the next k-step's decode), so the matrix core and the VALU overlap.
+template <int NMFMA>
+__device__ __forceinline__ void interleave_hint() {
+#pragma unroll
+  for (int i = 0; i < NMFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
+  }
+}
+
+// Direct global -> LDS copy of `bytes` (4 or 16) per lane; the LDS address
+// is the wave-uniform `lds` plus lane * bytes.  The builtin exists only for
+// the device; single-source compilation also runs a host pass over kernel
+// bodies, which must not see it (it would drop the kernels' host stubs).
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+#endif
+}
+
+__device__ __forceinline__ void lds_dma4(const void* g, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
+#endif
+}
+
+// Per-lane sources of one operand's stage loads: this wave's share of the
+// ROWS x 64 code bytes (16-byte chunks, LDS order) and ROWS x 8 scale bytes
+// (dwords).  Offsets are relative to the matrix base and exclude k0.
+template <int ROWS, int NWAVES>
+struct PipeLoader {
+  static constexpr int kCodeInsts = ROWS * 4 / 64 / NWAVES;   // per wave
+  static constexpr int kScaleInsts = ROWS * 2 / 64 / NWAVES;
+  static_assert(ROWS * 4 % (64 * NWAVES) == 0 && ROWS * 2 % (64 * NWAVES) == 0,
+                "tile rows must split evenly across the waves");
+  int64_t code_off[kCodeInsts];
+  int64_t scale_off[kScaleInsts];
+  // s_waitcnt immediate: vmcnt <= (loads of one stage of both operands),
+  // expcnt and lgkmcnt not waited (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
+  // lgkmcnt[11:8], vmcnt[5:4] at [15:14])
+  static constexpr int kStageLoads = 2 * (kCodeInsts + kScaleInsts);
+  static constexpr int kVmcntKeep = (kStageLoads & 0xF) | 0x70 | 0xF00 | ((kStageLoads >> 4) << 14);
+
+  __device__ __forceinline__ void init(int64_t row0, int64_t rows, int64_t k,
+                                       int wave, int lane) {
+    const int64_t kbytes = k / 2, kblocks = k / 16;
+#pragma unroll
+    for (int i = 0; i < kCodeInsts; ++i) {
+      const int q = (wave * kCodeInsts + i) * 64 + lane;   // LDS chunk
+      const int row = q >> 2;
+      const int part = (q & 3) ^ ((row >> 2) & 3);
+      const int64_t grow = row0 + row < rows ? row0 + row : rows - 1;
+      code_off[i] = grow * kbytes + part * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < kScaleInsts; ++j) {
+      const int d = (wave * kScaleInsts + j) * 64 + lane;  // LDS dword
+      const int row = d >> 1;
+      const int64_t grow = row0 + row < rows ? row0 + row : rows - 1;
+      scale_off[j] = grow * kblocks + (d & 1) * 4;
+    }
+  }
+
+  __device__ __forceinline__ void issue(const uint8_t* codes, const uint8_t* scales,
+                                        int64_t k0, uint8_t* lds_codes,
+                                        uint8_t* lds_scales, int wave) const {
+#pragma unroll
+    for (int i = 0; i < kCodeInsts; ++i)
+      lds_dma16(codes + code_off[i] + k0 / 2, lds_codes + (wave * kCodeInsts + i) * 1024);
+#pragma unroll
+    for (int j = 0; j < kScaleInsts; ++j)
+      lds_dma4(scales + scale_off[j] + k0 / 16, lds_scales + (wave * kScaleInsts + j) * 256);
+  }
+};
+
+// Workgroup barrier without the memory fence that __syncthreads() implies
+// (that fence waits for every outstanding load, including the LDS fill of a
+// later stage that is meant to stay in flight).  The wait for the stage
+// that must be resident is issued explicitly before this; the empty asm
+// statements keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// LDS ring of NS stages; each slot is a separate __shared__ object so that
+// the compiler can prove that filling one slot does not alias reads of the
+// others (it would otherwise wait for in-flight fills before every read).
+template <int NS>
+struct Ring {
+  uint8_t* a[NS];
+  uint8_t* b[NS];
+  uint8_t* sa[NS];
+  uint8_t* sb[NS];
+};
+
+// One K stage (BK = 128) of the pipelined main loop, consuming slot U.
+template <int U, int NS, int TM, int TN, int NW>
+__device__ __forceinline__ void pipe_stage(
+    const Ring<NS>& ring, int kt, int nk, float16_t (&acc)[TM][TN],
+    Operands<TM, TN>& cur, HalfFrags<TM>& fa, HalfFrags<TN>& fb,
+    const PipeLoader<TM * 64, NW>& la, const PipeLoader<TN * 64, NW>& lb,
+    const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+    const uint8_t* b_scales, int arow, int brow, int lane, int wave) {
+  constexpr int next = U == NS - 1 ? 0 : U + 1;
+  constexpr int fill_slot = U == 0 ? NS - 1 : U - 1;   // stage kt - 1's slot
+  const bool fill = kt + NS - 1 < nk;
+  if (fill) {
+    const int64_t k0 = static_cast<int64_t>(kt + NS - 1) * kBK;
+    la.issue(a_codes, a_scales, k0, ring.a[fill_slot], ring.sa[fill_slot], wave);
+    lb.issue(b_codes, b_scales, k0, ring.b[fill_slot], ring.sb[fill_slot], wave);
+  }
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    // fragments of the following half-stage (the next stage's first half
+    // when this is the second half; a resident slot is read even after the
+    // last stage, and never used)
+    HalfFrags<TM> na;
+    HalfFrags<TN> nb;
+    if (half == 0) {
+      na.read(ring.a[U], ring.sa[U], arow, lane, 1);
+      nb.read(ring.b[U], ring.sb[U], brow, lane, 1);
+    } else {
+      na.read(ring.a[next], ring.sa[next], arow, lane, 0);
+      nb.read(ring.b[next], ring.sb[next], brow, lane, 0);
+    }
+    PIPE_DS_HINT
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      Operands<TM, TN> nxt;
+      if (j < 3)
+        decode_step(nxt, fa, fb, j + 1);
+      else
+        decode_step(nxt, na, nb, 0);
+      mfma_step(acc, cur);
+      interleave_hint<TM * TN>();
+      cur = nxt;
+    }
+    fa = na;
+    fb = nb;
+  }
+  // stage kt + 1 must have landed before the barrier; the fill just issued
+  // for stage kt + NS - 1 may stay in flight (NS > 3)
+  if (NS > 3 && fill)
+    __builtin_amdgcn_s_waitcnt(PipeLoader<TM * 64, NW>::kVmcntKeep);
+  else
+    __builtin_amdgcn_s_waitcnt(0);
+  stage_barrier();
+}
+
+template <int WM, int WN, int TM, int TN, int OUT, int EPI>
+__global__ void __launch_bounds__(WM * WN * 64, 1)
+w4a4_gemm_pipelined(const uint8_t* __restrict__ a_codes,
+                    const uint8_t* __restrict__ a_scales,
+                    const float* __restrict__ a_global, int64_t m,
+                    const uint8_t* __restrict__ b_codes,
+                    const uint8_t* __restrict__ b_scales,
+                    const float* __restrict__ b_global, int64_t n, int64_t k,
+                    void* __restrict__ out, int64_t ldo, int tiles_m,
+                    int tiles_n) {
+  constexpr int NW = WM * WN;
+  constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+  constexpr int NS = PIPE_STAGES;
+  static_assert(NS >= 3 && NS <= 4, "ring depth");
+  static_assert(BM == TM * 64 && BN == TN * 64, "2 x 2 waves");
+  __shared__ __attribute__((aligned(1024))) uint8_t a0[BM * kPipeRowBytes], a1[BM * kPipeRowBytes],
+      a2[BM * kPipeRowBytes], a3[NS > 3 ? BM * kPipeRowBytes : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t b0[BN * kPipeRowBytes], b1[BN * kPipeRowBytes],
+      b2[BN * kPipeRowBytes], b3[NS > 3 ? BN * kPipeRowBytes : 16];
+  __shared__ __attribute__((aligned(256))) uint8_t sa0[BM * kPipeScaleBytes], sa1[BM * kPipeScaleBytes],
+      sa2[BM * kPipeScaleBytes], sa3[NS > 3 ? BM * kPipeScaleBytes : 16];
+  __shared__ __attribute__((aligned(256))) uint8_t sb0[BN * kPipeScaleBytes], sb1[BN * kPipeScaleBytes],
+      sb2[BN * kPipeScaleBytes], sb3[NS > 3 ? BN * kPipeScaleBytes : 16];
+  Ring<NS> ring;
+  {
+    uint8_t* const as[4] = {a0, a1, a2, a3};
+    uint8_t* const bs[4] = {b0, b1, b2, b3};
+    uint8_t* const sas[4] = {sa0, sa1, sa2, sa3};
+    uint8_t* const sbs[4] = {sb0, sb1, sb2, sb3};
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      ring.a[i] = as[i];
+      ring.b[i] = bs[i];
+      ring.sa[i] = sas[i];
+      ring.sb[i] = sbs[i];
+    }
+  }
+
+  const int ntiles = tiles_m * tiles_n;
+  int bid = blockIdx.x;
+  if (ntiles % 8 == 0) bid = (bid % 8) * (ntiles / 8) + bid / 8;
+  constexpr int kGroup = 8;
+  const int group = bid / (kGroup * tiles_n);
+  const int first_m = group * kGroup;
+  const int gm = min(tiles_m - first_m, kGroup);
+  const int tile_m = first_m + (bid % (kGroup * tiles_n)) % gm;
+  const int tile_n = (bid % (kGroup * tiles_n)) / gm;
+  const int64_t m0 = static_cast<int64_t>(tile_m) * BM;
+  const int64_t n0 = static_cast<int64_t>(tile_n) * BN;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int arow = wm * TM * 32, brow = wn * TN * 32;
+
+  float16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  const int nk = static_cast<int>(k / kBK);
+  PipeLoader<BM, NW> la;
+  PipeLoader<BN, NW> lb;
+  la.init(m0, m, k, wave, lane);
+  lb.init(n0, n, k, wave, lane);
+  // prologue: stages 0 .. NS-2 into slots 0 .. NS-2
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st) {
+    if (st < nk) {
+      la.issue(a_codes, a_scales, static_cast<int64_t>(st) * kBK, ring.a[st], ring.sa[st], wave);
+      lb.issue(b_codes, b_scales, static_cast<int64_t>(st) * kBK, ring.b[st], ring.sb[st], wave);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // all of this lane's loads have landed
+  stage_barrier();
+
+  HalfFrags<TM> fa;
+  HalfFrags<TN> fb;
+  fa.read(ring.a[0], ring.sa[0], arow, lane, 0);
+  fb.read(ring.b[0], ring.sb[0], brow, lane, 0);
+  Operands<TM, TN> cur;
+  decode_step(cur, fa, fb, 0);
+
+  // The stage loop is unrolled by the ring depth so that each stage reads
+  // and fills slots known at compile time.
+  for (int kt0 = 0; kt0 < nk; kt0 += NS) {
+#define NVFP4_PIPE_STAGE(U)                                                    \
+    if (kt0 + U < nk)                                                          \
+      pipe_stage<U, NS, TM, TN, NW>(ring, kt0 + U, nk, acc, cur, fa, fb, la, lb, \
+                                    a_codes, a_scales, b_codes, b_scales,      \
+                                    arow, brow, lane, wave);
+    NVFP4_PIPE_STAGE(0)
+    NVFP4_PIPE_STAGE(1)
+    NVFP4_PIPE_STAGE(2)
+    if constexpr (NS > 3) { NVFP4_PIPE_STAGE(3) }
+#undef NVFP4_PIPE_STAGE
+  }
+
+  const double gab = static_cast<double>(*a_global) * static_cast<double>(*b_global);
+  const int col_l = lane & 31, row_l = (lane >> 5) * 4;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int64_t col = n0 + brow + j * 32 + col_l;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = m0 + arow + i * 32 + 8 * (e >> 2) + row_l + (e & 3);
+        if (row < m && col < n) {
+          const float y = epilogue<EPI>(static_cast<float>(static_cast<double>(acc[i][j][e]) * gab));
+          if constexpr (OUT == kOutF32)
+            static_cast<float*>(out)[row * ldo + col] = y;
+          else
+            static_cast<unsigned short*>(out)[row * ldo + col] = f32_to_bf16_rne(y);
+        }
+      }
+    }
+}
+
+template <int WM, int WN, int TM, int TN, int OUT, int EPI>
+hipError_t launch_pipelined(const uint8_t* a_codes, const uint8_t* a_scales,
+                            const float* a_global, int64_t m,
+                            const uint8_t* b_codes, const uint8_t* b_scales,
+                            const float* b_global, int64_t n, int64_t k,
+                            void* out, int64_t ldo, hipStream_t stream) {
+  constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+  const int64_t tm = (m + BM - 1) / BM, tn = (n + BN - 1) / BN;
+  if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
+  w4a4_gemm_pipelined<WM, WN, TM, TN, OUT, EPI>
+      <<<static_cast<unsigned>(tm * tn), WM * WN * 64, 0, stream>>>(
+          a_codes, a_scales, a_global, m, b_codes, b_scales, b_global, n, k,
+          out, ldo, static_cast<int>(tm), static_cast<int>(tn));
+  return hipGetLastError();
+}
+
 template <int WM, int WN, int TM, int TN, bool ALIGNED, int OUT, int EPI>
 hipError_t launch_cfg(const uint8_t* a_codes, const uint8_t* a_scales,
                       const float* a_global, int64_t m,
@@ -326,6 +739,12 @@ hipError_t dispatch_shape(const uint8_t* a_codes, const uint8_t* a_scales,
                           const uint8_t* b_codes, const uint8_t* b_scales,
                           const float* b_global, int64_t n, int64_t k,
                           void* out, int64_t ldo, hipStream_t stream) {
+  if constexpr (ALIGNED) {
+    if (m >= 256 && n >= 256)
+      return launch_pipelined<2, 2, 4, 4, OUT, EPI>(
+          a_codes, a_scales, a_global, m, b_codes, b_scales, b_global, n, k,
+          out, ldo, stream);
+  }
   return launch_cfg<2, 2, 4, 4, ALIGNED, OUT, EPI>(
       a_codes, a_scales, a_global, m, b_codes, b_scales, b_global, n, k, out,
       ldo, stream);
@@ -337,8 +756,9 @@ hipError_t dispatch_align(const uint8_t* a_codes, const uint8_t* a_scales,
                           const uint8_t* b_codes, const uint8_t* b_scales,
                           const float* b_global, int64_t n, int64_t k,
                           void* out, int64_t ldo, hipStream_t stream) {
-  // 16-byte code loads need 16-byte aligned rows
-  const bool aligned = (k / 2) % 16 == 0;
+  // whole stages (k % 128 == 0): unconditional 16-byte code loads and
+  // 8-byte scale loads
+  const bool aligned = k % kBK == 0;
   if (aligned)
     return dispatch_shape<true, OUT, EPI>(a_codes, a_scales, a_global, m,
                                           b_codes, b_scales, b_global, n, k,
