@@ -42,6 +42,9 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--workloads", action=argparse.BooleanOptionalAction,
+                   default=True, help="also time the other four workloads "
+                   "once each (reported, not part of the step)")
     return p.parse_args()
 
 
@@ -104,6 +107,105 @@ def cpu_baseline():
         "quantize_gbps": xv.size * 2.5625 / tq / 1e9,
         "gemm_tflops": 2.0 * GM * GN * K / tg / 1e12,
     }
+
+
+def _time(fn, reps, stream):
+    """Average GPU time (us) of fn() over reps launches (HIP events on the
+    launch stream), after one warm-up call."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def other_workloads(nv, synth, dev, stream, reps=10):
+    """Kernel timings of the other workloads at hidden size 5120 (inputs
+    resident in HBM): in_proj 4096x12288, gate projections 32768x64 with
+    alpha/beta epilogues, a harmonised fused group (N = 17536), the tiny
+    16x128x256 case, and the self-calibrated (COMPUTE) activation quantize."""
+    import numpy as np
+    import torch
+
+    def up(w, name):
+        v, b, dt = synth.workload_tensor(w, name)
+        if dt == "f32":
+            return torch.from_numpy(v).to(dev)
+        return torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    out = {}
+    # in_proj: X[4096x5120], W[12288x5120]
+    x, w = up(2, "x"), up(2, "w")
+    qx, qw = nv.quantize(x), nv.quantize(w)
+    gx = qx.global_scale.clone()
+    t_q = _time(lambda: nv.quantize(x, global_scale=gx, out=(qx.codes, qx.scales)), reps, stream)
+    t_qw = _time(lambda: nv.quantize(w, out=(qw.codes, qw.scales)), reps, stream)
+    y = torch.empty((4096, 12288), dtype=torch.bfloat16, device=dev)
+    t_g = _time(lambda: nv.gemm(qx, qw, out_dtype=torch.bfloat16, out=y), reps, stream)
+    fl = 2.0 * 4096 * 12288 * 5120
+    out["in_proj_4096x12288x5120"] = {
+        "quantize_x_us": t_q, "quantize_x_gbps": 4096 * 5120 * 2.5625 / t_q / 1e3,
+        "quantize_w_compute_us": t_qw,
+        "gemm_us": t_g, "gemm_tflops": fl / t_g / 1e6}
+    del x, w, qx, qw, y
+    # gate projections: X[32768x5120], W_a/W_b[64x5120], fp32 out + gates
+    x = up(3, "x")
+    qx = nv.quantize(x)
+    res = {}
+    for name, epi in (("w_a", "alpha"), ("w_b", "beta")):
+        qw = nv.quantize(up(3, name))
+        y = torch.empty((32768, 64), dtype=torch.float32, device=dev)
+        t = _time(lambda: nv.gemm(qx, qw, out_dtype=torch.float32, epilogue=epi, out=y), reps, stream)
+        byts = 32768 * 5120 * 0.5625 + 64 * 5120 * 0.5625 + 32768 * 64 * 4
+        res[name + "_" + epi] = {"gemm_us": t, "gbps": byts / t / 1e3,
+                                 "frac_hbm_peak": byts / t / 1e3 / PEAK_HBM_GBPS}
+    out["gate_proj_32768x64x5120"] = res
+    del x, qx
+    # harmonised fused group 12288|5120|128 with X[8192x5120]
+    sizes = [12288, 5120, 128]
+    offs = [0, 12288, 17408, 17536]
+    codes = torch.empty((17536, 2560), dtype=torch.uint8, device=dev)
+    scales = torch.empty((17536, 320), dtype=torch.uint8, device=dev)
+    gmod = torch.empty(3, dtype=torch.float32, device=dev)
+    for i, nm in enumerate(("w1", "w2", "w3")):
+        q = nv.quantize(up(4, nm), out=(codes[offs[i]:offs[i + 1]], scales[offs[i]:offs[i + 1]]))
+        gmod[i:i + 1].copy_(q.global_scale)
+    saved = scales.clone()
+
+    def harm():
+        scales.copy_(saved)
+        return nv.harmonize_group(scales, 5120, offs, gmod)
+    t_copy = _time(lambda: scales.copy_(saved), reps, stream)
+    t_h = _time(harm, reps, stream) - t_copy
+    gstar = harm()
+    x = up(4, "x")
+    qx = nv.quantize(x)
+    y = torch.empty((8192, 17536), dtype=torch.bfloat16, device=dev)
+    wq = nv.NVFP4(codes, scales, gstar)
+    t_g = _time(lambda: nv.gemm(qx, wq, out_dtype=torch.bfloat16, out=y), reps, stream)
+    out["fused_group_8192x17536x5120"] = {
+        "harmonize_us": t_h, "gemm_us": t_g,
+        "gemm_tflops": 2.0 * 8192 * 17536 * 5120 / t_g / 1e6}
+    del x, qx, y, codes, scales
+    # tiny: 16x128x256 fp32
+    x, w = up(1, "x"), up(1, "w")
+    qx, qw = nv.quantize(x), nv.quantize(w)
+    t_q = _time(lambda: nv.quantize(x), reps, stream)
+    t_g = _time(lambda: nv.gemm(qx, qw, out_dtype=torch.float32), reps, stream)
+    out["tiny_16x128x256"] = {"quantize_compute_us": t_q, "gemm_us": t_g}
+    # self-calibrated quantize of the long-prefill activations
+    xv = up(5, "x")
+    q = nv.quantize(xv)
+    t_c = _time(lambda: nv.quantize(xv, out=(q.codes, q.scales)), reps, stream)
+    out["quantize_compute_32768x5120"] = {
+        "us": t_c, "gbps_4.5625B_per_elem": 32768 * 5120 * 4.5625 / t_c / 1e3}
+    return out
 
 
 def main():
@@ -207,6 +309,7 @@ def main():
     parity_ok = bool(np.all(np.abs(got - ref16) <= np.abs(ref16) * 2.0 ** -7
                             + 1e-30))
 
+    reported = other_workloads(nv, synth, dev, stream) if args.workloads else {}
     traffic = measured_traffic("w4a4_gemm_prefill_32768x10240x5120_traffic.md",
                                1)
     out = {
@@ -249,6 +352,7 @@ def main():
                             PEAK_HBM_GBPS},
         },
         "parity_sample_ok": parity_ok,
+        "other_workloads": reported,
         "kernel_sources_sha256_16": {s: source_hash(s)
                                      for s in KERNEL_SOURCES},
     }

@@ -717,6 +717,172 @@ hipError_t launch_pipelined(const uint8_t* a_codes, const uint8_t* a_scales,
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Skinny kernel: one operand has at most 64 rows (decode batches, the
+// per-head gate projections).  The other operand streams from HBM once, so
+// the shape is bandwidth-bound: there is no LDS staging; each lane loads
+// its own 16 code bytes (32 K of one row) and 2 block scales per 64-K chunk
+// straight into registers, several chunks in flight.  A workgroup owns one
+// TMT x TNT grid of 32 x 32 output tiles and its 4 waves split K; the
+// partial accumulators are summed through LDS before the epilogue.  Rows
+// past m or n read a clamped valid row and are never stored.
+// Requires k % 64 == 0.
+
+constexpr int kSkinnyWaves = 4;
+constexpr int kSkinnyUnroll = 4;   // 64-K chunks in flight per lane
+
+struct ChunkFrag {
+  uint4 code;        // 32 K of one row (this lane's half of a 64-K chunk)
+  unsigned short sc; // its two E4M3 block scales
+};
+
+__device__ __forceinline__ ChunkFrag load_chunk(const uint8_t* __restrict__ codes,
+                                                const uint8_t* __restrict__ scales,
+                                                int64_t row, int64_t kbytes,
+                                                int64_t kblocks, int64_t chunk,
+                                                int h) {
+  ChunkFrag f;
+  f.code = *reinterpret_cast<const uint4*>(codes + row * kbytes + chunk * 32 + h * 16);
+  f.sc = *reinterpret_cast<const unsigned short*>(scales + row * kblocks + chunk * 4 + h * 2);
+  return f;
+}
+
+// operand of k-step j (0..3) of a chunk: codes dword j, block j / 2
+__device__ __forceinline__ half8_t chunk_operand(const ChunkFrag& f, unsigned sc2, int j) {
+  const unsigned w = j == 0 ? f.code.x : j == 1 ? f.code.y : j == 2 ? f.code.z : f.code.w;
+  const unsigned short sb = (j >> 1) ? static_cast<unsigned short>(sc2 >> 16)
+                                     : static_cast<unsigned short>(sc2 & 0xFFFFu);
+  const _Float16 sv = __builtin_bit_cast(_Float16, sb);
+  half2_t s;
+  s[0] = sv;
+  s[1] = sv;
+  return decode8(w, s);
+}
+
+template <int TMT, int TNT, int OUT, int EPI>
+__global__ void __launch_bounds__(kSkinnyWaves * 64)
+w4a4_gemm_skinny(const uint8_t* __restrict__ a_codes,
+                 const uint8_t* __restrict__ a_scales,
+                 const float* __restrict__ a_global, int64_t m,
+                 const uint8_t* __restrict__ b_codes,
+                 const uint8_t* __restrict__ b_scales,
+                 const float* __restrict__ b_global, int64_t n, int64_t k,
+                 void* __restrict__ out, int64_t ldo, int tiles_n) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 31, h = lane >> 5;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x / tiles_n) * (32 * TMT);
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x % tiles_n) * (32 * TNT);
+  const int64_t kbytes = k / 2, kblocks = k / 16;
+  const int64_t nchunks = k / 64;
+
+  int64_t arow[TMT], brow[TNT];
+#pragma unroll
+  for (int i = 0; i < TMT; ++i) {
+    const int64_t g = m0 + i * 32 + r;
+    arow[i] = g < m ? g : m - 1;
+  }
+#pragma unroll
+  for (int j = 0; j < TNT; ++j) {
+    const int64_t g = n0 + j * 32 + r;
+    brow[j] = g < n ? g : n - 1;
+  }
+
+  float16_t acc[TMT][TNT];
+#pragma unroll
+  for (int i = 0; i < TMT; ++i)
+#pragma unroll
+    for (int j = 0; j < TNT; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  // wave w takes chunks w, w + 4, w + 8, ...
+  for (int64_t c0 = wave; c0 < nchunks; c0 += kSkinnyWaves * kSkinnyUnroll) {
+    ChunkFrag fa[kSkinnyUnroll][TMT], fb[kSkinnyUnroll][TNT];
+#pragma unroll
+    for (int u = 0; u < kSkinnyUnroll; ++u) {
+      const int64_t c = c0 + u * kSkinnyWaves;
+      const int64_t cc = c < nchunks ? c : nchunks - 1;   // clamped, unused
+#pragma unroll
+      for (int i = 0; i < TMT; ++i) fa[u][i] = load_chunk(a_codes, a_scales, arow[i], kbytes, kblocks, cc, h);
+#pragma unroll
+      for (int j = 0; j < TNT; ++j) fb[u][j] = load_chunk(b_codes, b_scales, brow[j], kbytes, kblocks, cc, h);
+    }
+    // every chunk is computed; a chunk past k (clamped load) gets block
+    // scale 0, so all its products are exactly 0
+#pragma unroll
+    for (int u = 0; u < kSkinnyUnroll; ++u) {
+      const bool valid = c0 + u * kSkinnyWaves < nchunks;
+      unsigned sa[TMT], sb[TNT];
+#pragma unroll
+      for (int i = 0; i < TMT; ++i)
+        sa[i] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+                    valid ? fa[u][i].sc : 0u, 1.0f, false));
+#pragma unroll
+      for (int j = 0; j < TNT; ++j)
+        sb[j] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+                    valid ? fb[u][j].sc : 0u, 1.0f, false));
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        half8_t av[TMT], bv[TNT];
+#pragma unroll
+        for (int i = 0; i < TMT; ++i) av[i] = chunk_operand(fa[u][i], sa[i], ks);
+#pragma unroll
+        for (int j = 0; j < TNT; ++j) bv[j] = chunk_operand(fb[u][j], sb[j], ks);
+#pragma unroll
+        for (int i = 0; i < TMT; ++i)
+#pragma unroll
+          for (int j = 0; j < TNT; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+
+  // sum the waves' partial accumulators: red[wave][tile][e][lane]
+  __shared__ float red[kSkinnyWaves][TMT * TNT][16][64];
+#pragma unroll
+  for (int i = 0; i < TMT; ++i)
+#pragma unroll
+    for (int j = 0; j < TNT; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red[wave][i * TNT + j][e][lane] = acc[i][j][e];
+  __syncthreads();
+  const double gab = static_cast<double>(*a_global) * static_cast<double>(*b_global);
+  constexpr int kVals = TMT * TNT * 16 * 64;
+#pragma unroll
+  for (int v0 = 0; v0 < kVals; v0 += kSkinnyWaves * 64) {
+    const int v = v0 + threadIdx.x;
+    const int l = v & 63, e = (v >> 6) & 15, t = v >> 10;
+    float sum = red[0][t][e][l];
+#pragma unroll
+    for (int w = 1; w < kSkinnyWaves; ++w) sum += red[w][t][e][l];
+    const int ti = t / TNT, tj = t % TNT;
+    const int64_t row = m0 + ti * 32 + 8 * (e >> 2) + (l >> 5) * 4 + (e & 3);
+    const int64_t col = n0 + tj * 32 + (l & 31);
+    if (row < m && col < n) {
+      const float y = epilogue<EPI>(static_cast<float>(static_cast<double>(sum) * gab));
+      if constexpr (OUT == kOutF32)
+        static_cast<float*>(out)[row * ldo + col] = y;
+      else
+        static_cast<unsigned short*>(out)[row * ldo + col] = f32_to_bf16_rne(y);
+    }
+  }
+}
+
+template <int TMT, int TNT, int OUT, int EPI>
+hipError_t launch_skinny(const uint8_t* a_codes, const uint8_t* a_scales,
+                         const float* a_global, int64_t m,
+                         const uint8_t* b_codes, const uint8_t* b_scales,
+                         const float* b_global, int64_t n, int64_t k,
+                         void* out, int64_t ldo, hipStream_t stream) {
+  const int64_t tm = (m + 32 * TMT - 1) / (32 * TMT), tn = (n + 32 * TNT - 1) / (32 * TNT);
+  if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
+  w4a4_gemm_skinny<TMT, TNT, OUT, EPI>
+      <<<static_cast<unsigned>(tm * tn), kSkinnyWaves * 64, 0, stream>>>(
+          a_codes, a_scales, a_global, m, b_codes, b_scales, b_global, n, k,
+          out, ldo, static_cast<int>(tn));
+  return hipGetLastError();
+}
+
 template <int WM, int WN, int TM, int TN, bool ALIGNED, int OUT, int EPI>
 hipError_t launch_cfg(const uint8_t* a_codes, const uint8_t* a_scales,
                       const float* a_global, int64_t m,
@@ -739,15 +905,18 @@ hipError_t dispatch_shape(const uint8_t* a_codes, const uint8_t* a_scales,
                           const uint8_t* b_codes, const uint8_t* b_scales,
                           const float* b_global, int64_t n, int64_t k,
                           void* out, int64_t ldo, hipStream_t stream) {
+#define NVFP4_ARGS a_codes, a_scales, a_global, m, b_codes, b_scales, b_global, \
+                   n, k, out, ldo, stream
   if constexpr (ALIGNED) {
-    if (m >= 256 && n >= 256)
-      return launch_pipelined<2, 2, 4, 4, OUT, EPI>(
-          a_codes, a_scales, a_global, m, b_codes, b_scales, b_global, n, k,
-          out, ldo, stream);
+    // k % 128 == 0 here, so the skinny kernel's 64-K chunks tile k
+    if (m <= 32) return launch_skinny<1, 1, OUT, EPI>(NVFP4_ARGS);
+    if (m <= 64) return launch_skinny<2, 1, OUT, EPI>(NVFP4_ARGS);
+    if (n <= 32) return launch_skinny<1, 1, OUT, EPI>(NVFP4_ARGS);
+    if (n <= 64) return launch_skinny<1, 2, OUT, EPI>(NVFP4_ARGS);
+    return launch_pipelined<2, 2, 4, 4, OUT, EPI>(NVFP4_ARGS);
   }
-  return launch_cfg<2, 2, 4, 4, ALIGNED, OUT, EPI>(
-      a_codes, a_scales, a_global, m, b_codes, b_scales, b_global, n, k, out,
-      ldo, stream);
+  return launch_cfg<2, 2, 4, 4, ALIGNED, OUT, EPI>(NVFP4_ARGS);
+#undef NVFP4_ARGS
 }
 
 template <int OUT, int EPI>

@@ -312,7 +312,9 @@ def test_gemm_tiny_exact(out_dtype):
 
 @pytest.mark.parametrize("m,n,k", [(1, 1, 16), (33, 65, 48), (300, 130, 272),
                                    (17, 300, 5136), (257, 513, 1024),
-                                   (64, 64, 4096)])
+                                   (64, 64, 4096), (300, 20, 1024),
+                                   (40, 1000, 512), (1000, 50, 256),
+                                   (7, 777, 384), (513, 257, 640)])
 def test_gemm_ragged_shapes(m, n, k):
     rng = np.random.default_rng(m * 31 + n * 7 + k)
     xv = rng.standard_normal((m, k)).astype(np.float32)
