@@ -42,6 +42,9 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="after the timed steps, copy a 512 MiB device buffer "
+                   "once (a known-size kernel for scaling HBM counters)")
     p.add_argument("--workloads", action=argparse.BooleanOptionalAction,
                    default=True, help="also time the other four workloads "
                    "once each (reported, not part of the step)")
@@ -287,6 +290,12 @@ def main():
     print("[bench] timed %d steps in %.3f s" % (args.steps, elapsed),
           file=sys.stderr, flush=True)
 
+    if args.copy_calibration:
+        src = torch.ones(512 * 2 ** 20 // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     avg_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]]))
               for n in names}
     flops_gemm = 2.0 * M * N * K
