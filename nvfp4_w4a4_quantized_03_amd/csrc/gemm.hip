@@ -71,9 +71,10 @@ __device__ __forceinline__ unsigned short f32_to_bf16_rne(float f) {
 template <int EPI>
 __device__ __forceinline__ float epilogue(float y) {
   if constexpr (EPI == kEpiAlpha) {
-    // exp(-softplus(y)), softplus(y) = max(y, 0) + log1p(exp(-|y|))
-    const float sp = fmaxf(y, 0.0f) + log1pf(expf(-fabsf(y)));
-    return expf(-sp);
+    // exp(-softplus(y)) = exp(-log(1 + e^y)) = 1 / (1 + e^y); the short form
+    // keeps the epilogue small enough to unroll over the accumulator tiles
+    // (which must stay in registers).  e^y overflowing to inf gives 0.
+    return 1.0f / (1.0f + expf(y));
   } else if constexpr (EPI == kEpiBeta) {
     return 1.0f / (1.0f + expf(-y));
   } else {
@@ -345,22 +346,25 @@ w4a4_gemm_kernel(const uint8_t* __restrict__ a_codes,
 // ---------------------------------------------------------------------------
 // Pipelined kernel for large, whole-stage shapes (k % 128 == 0).
 //
-// * Operand stages go from global memory straight into LDS (gfx950
-//   global_load_lds_dwordx4 / _dword: no staging registers, no LDS store
-//   instructions).  Codes are stored unpadded, 64 bytes per row per stage,
-//   with the four 16-byte chunks of row r permuted by XOR with (r / 4) % 4 so
-//   that 16 lanes reading 16 consecutive rows hit 16 distinct bank groups.
-//   Scales stay raw E4M3 (8 bytes per row per stage) and are widened to
-//   fp16 when a fragment is read.
-// * Three LDS stages form a ring: stage kt + 2 is fetched while stage kt is
-//   consumed, and stage kt + 1 is already resident, so the next half-stage's
-//   fragments are read one half ahead and the next k-step's operands are
-//   decoded while the 16 MFMAs of the current k-step issue.  One wait for the
-//   stage's own loads and one barrier per stage keep the ring ordered: stage
-//   kt + 2 goes into the slot of stage kt - 1, which every wave finished
+// * Operand stages go from global memory straight into LDS with buffer
+//   loads (buffer_load_dwordx4 / _dword ... lds: no staging registers, no
+//   LDS store instructions).  Codes are stored unpadded, 64 bytes per row per
+//   stage, with the four 16-byte chunks of row r permuted by XOR with
+//   (r / 4) % 4 so that 16 lanes reading 16 consecutive rows hit 16 distinct
+//   bank groups.  Scales stay raw E4M3 (8 bytes per row per stage) and are
+//   widened to fp16 when an operand is decoded.
+// * NS = 4 LDS slots form a ring: stages kt + 1 .. kt + 3 are in flight or
+//   resident while stage kt is consumed, so the next half-stage's fragments
+//   are read one half ahead and the next k-step's operands are decoded while
+//   the 16 MFMAs of the current k-step issue.  Each stage issues the same
+//   loads (past the last stage they repeat it into the slot just freed),
+//   spread over its first k-step's MFMAs; one wait that leaves the two newest
+//   fills in flight and one barrier per stage keep the ring ordered: stage
+//   kt + 3 goes into the slot of stage kt - 1, which every wave finished
 //   before the barrier that closed stage kt - 1.
 // * Rows past m or n load a clamped (valid) row; their outputs are never
-//   stored.
+//   stored.  Offsets within a tile are 32-bit, so the launcher takes this
+//   kernel only for k <= 2^22.
 
 constexpr int kPipeRowBytes = kCodeBytes;        // 64, unpadded
 constexpr int kPipeScaleBytes = kScalesPerRow;   // 8 raw E4M3 bytes
@@ -370,7 +374,9 @@ __device__ __forceinline__ int pipe_chunk(int row, int part) {
 }
 
 // A wave's fragments for one half-stage (4 k-steps, 64 K per lane half):
-// per 32-row tile, 16 code bytes and the two fp16 scales of its blocks.
+// per 32-row tile, 16 code bytes and the two raw E4M3 scales of its blocks
+// (low 16 bits).  The scales are widened to fp16 only when an operand is
+// decoded, so that nothing consumes a fragment right after its LDS read.
 template <int T>
 struct HalfFrags {
   uint4 code[T];
@@ -384,9 +390,7 @@ struct HalfFrags {
     for (int t = 0; t < T; ++t) {
       const int row = row_base + t * 32 + r;
       code[t] = *reinterpret_cast<const uint4*>(lds_codes + pipe_chunk(row, 2 * h + half) * 16);
-      const unsigned raw = *reinterpret_cast<const unsigned*>(lds_scales + row * kPipeScaleBytes + 4 * h);
-      scale[t] = half ? __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw, 1.0f, true))
-                      : __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw, 1.0f, false));
+      scale[t] = *reinterpret_cast<const unsigned short*>(lds_scales + row * kPipeScaleBytes + 4 * h + 2 * half);
     }
   }
 
@@ -394,8 +398,9 @@ struct HalfFrags {
   __device__ __forceinline__ half8_t operand(int t, int j) const {
     const uint4 q = code[t];
     const unsigned w = j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
-    const unsigned short sb = (j >> 1) ? static_cast<unsigned short>(scale[t] >> 16)
-                                       : static_cast<unsigned short>(scale[t] & 0xFFFFu);
+    const unsigned wide = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scale[t], 1.0f, false));
+    const unsigned short sb = (j >> 1) ? static_cast<unsigned short>(wide >> 16)
+                                       : static_cast<unsigned short>(wide & 0xFFFFu);
     const _Float16 sv = __builtin_bit_cast(_Float16, sb);
     half2_t sc;
     sc[0] = sv;
@@ -430,29 +435,43 @@ __device__ __forceinline__ void mfma_step(float16_t (&acc)[TM][TN], const Operan
 
 // Scheduling hint for one k-step: alternate one MFMA with a few VALU ops
 // (the next k-step's decode), so the matrix core and the VALU overlap.
-template <int NMFMA>
+template <int NMFMA, int NVMEM = 0>
 __device__ __forceinline__ void interleave_hint() {
 #pragma unroll
   for (int i = 0; i < NMFMA; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
     __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
+    if (i < NVMEM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
   }
 }
 
-// Direct global -> LDS copy of `bytes` (4 or 16) per lane; the LDS address
-// is the wave-uniform `lds` plus lane * bytes.  The builtin exists only for
-// the device; single-source compilation also runs a host pass over kernel
-// bodies, which must not see it (it would drop the kernels' host stubs).
-__device__ __forceinline__ void lds_dma16(const void* g, void* lds) {
+// Buffer loads of 16 or 4 bytes per lane straight into LDS, at the
+// wave-uniform `lds` plus lane * size; the source is the resource base +
+// voff + soff.  Buffer (not FLAT-encoded global) loads are used so that the
+// compiler can keep counting LDS reads in order while these are in flight:
+// a pending FLAT load may touch LDS, which makes every later LDS-read wait a
+// full drain.
+__device__ __forceinline__ void lds_buf16(__amdgpu_buffer_rsrc_t rsrc, void* lds,
+                                          unsigned voff, unsigned soff) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rsrc, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 #endif
 }
 
-__device__ __forceinline__ void lds_dma4(const void* g, void* lds) {
+__device__ __forceinline__ void lds_buf4(__amdgpu_buffer_rsrc_t rsrc, void* lds,
+                                         unsigned voff, unsigned soff) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rsrc, (__attribute__((address_space(3))) void*)lds, 4, voff, soff, 0, 0);
 #endif
+}
+
+// s_waitcnt immediate that waits until at most `keep` vector-memory ops are
+// outstanding, without waiting on expcnt/lgkmcnt (gfx9 encoding: vmcnt[3:0],
+// expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] at [15:14]).
+constexpr int kVmcntKeepOf(int keep) {
+  return (keep & 0xF) | 0x70 | 0xF00 | ((keep >> 4) << 14);
 }
 
 // Per-lane sources of one operand's stage loads: this wave's share of the
@@ -464,43 +483,49 @@ struct PipeLoader {
   static constexpr int kScaleInsts = ROWS * 2 / 64 / NWAVES;
   static_assert(ROWS * 4 % (64 * NWAVES) == 0 && ROWS * 2 % (64 * NWAVES) == 0,
                 "tile rows must split evenly across the waves");
-  int64_t code_off[kCodeInsts];
-  int64_t scale_off[kScaleInsts];
-  // s_waitcnt immediate: vmcnt <= (loads of one stage of both operands),
-  // expcnt and lgkmcnt not waited (gfx9 encoding: vmcnt[3:0], expcnt[6:4],
-  // lgkmcnt[11:8], vmcnt[5:4] at [15:14])
-  static constexpr int kStageLoads = 2 * (kCodeInsts + kScaleInsts);
-  static constexpr int kVmcntKeep = (kStageLoads & 0xF) | 0x70 | 0xF00 | ((kStageLoads >> 4) << 14);
+  static constexpr int kIssues = kCodeInsts + kScaleInsts;   // per wave per stage
+  __amdgpu_buffer_rsrc_t code_rsrc, scale_rsrc;
+  unsigned code_off[kCodeInsts];
+  unsigned scale_off[kScaleInsts];
 
-  __device__ __forceinline__ void init(int64_t row0, int64_t rows, int64_t k,
+  // Offsets are 32-bit and relative to the tile's first row, so the tile's
+  // rows times k / 2 bytes must stay below 2^32 (the launcher checks k).
+  __device__ __forceinline__ void init(const uint8_t* codes, const uint8_t* scales,
+                                       int64_t row0, int64_t rows, int64_t k,
                                        int wave, int lane) {
     const int64_t kbytes = k / 2, kblocks = k / 16;
+    const int last = static_cast<int>(rows - 1 - row0 < ROWS - 1 ? rows - 1 - row0 : ROWS - 1);
+    code_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(codes + row0 * kbytes), 0,
+        static_cast<int>((last + 1) * kbytes), 0x00020000);
+    scale_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(scales + row0 * kblocks), 0,
+        static_cast<int>((last + 1) * kblocks), 0x00020000);
 #pragma unroll
     for (int i = 0; i < kCodeInsts; ++i) {
       const int q = (wave * kCodeInsts + i) * 64 + lane;   // LDS chunk
       const int row = q >> 2;
       const int part = (q & 3) ^ ((row >> 2) & 3);
-      const int64_t grow = row0 + row < rows ? row0 + row : rows - 1;
-      code_off[i] = grow * kbytes + part * 16;
+      code_off[i] = static_cast<unsigned>((row < last ? row : last) * kbytes + part * 16);
     }
 #pragma unroll
     for (int j = 0; j < kScaleInsts; ++j) {
       const int d = (wave * kScaleInsts + j) * 64 + lane;  // LDS dword
       const int row = d >> 1;
-      const int64_t grow = row0 + row < rows ? row0 + row : rows - 1;
-      scale_off[j] = grow * kblocks + (d & 1) * 4;
+      scale_off[j] = static_cast<unsigned>((row < last ? row : last) * kblocks + (d & 1) * 4);
     }
   }
 
-  __device__ __forceinline__ void issue(const uint8_t* codes, const uint8_t* scales,
-                                        int64_t k0, uint8_t* lds_codes,
+  __device__ __forceinline__ void issue(int64_t k0, uint8_t* lds_codes,
                                         uint8_t* lds_scales, int wave) const {
 #pragma unroll
     for (int i = 0; i < kCodeInsts; ++i)
-      lds_dma16(codes + code_off[i] + k0 / 2, lds_codes + (wave * kCodeInsts + i) * 1024);
+      lds_buf16(code_rsrc, lds_codes + (wave * kCodeInsts + i) * 1024, code_off[i],
+                static_cast<unsigned>(k0 / 2));
 #pragma unroll
     for (int j = 0; j < kScaleInsts; ++j)
-      lds_dma4(scales + scale_off[j] + k0 / 16, lds_scales + (wave * kScaleInsts + j) * 256);
+      lds_buf4(scale_rsrc, lds_scales + (wave * kScaleInsts + j) * 256, scale_off[j],
+               static_cast<unsigned>(k0 / 16));
   }
 };
 
@@ -515,9 +540,10 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// LDS ring of NS stages; each slot is a separate __shared__ object so that
-// the compiler can prove that filling one slot does not alias reads of the
-// others (it would otherwise wait for in-flight fills before every read).
+// LDS ring of NS stages; each slot is a separate __shared__ object (holding
+// A codes, B codes, A scales, B scales) so that the compiler can prove that
+// filling one slot does not alias reads of the others (it would otherwise
+// wait for in-flight fills before every read).
 template <int NS>
 struct Ring {
   uint8_t* a[NS];
@@ -527,20 +553,24 @@ struct Ring {
 };
 
 // One K stage (BK = 128) of the pipelined main loop, consuming slot U.
-template <int U, int NS, int TM, int TN, int NW>
+template <int U, int NS, int TM, int TN, int NW, int BM, int BN>
 __device__ __forceinline__ void pipe_stage(
     const Ring<NS>& ring, int kt, int nk, float16_t (&acc)[TM][TN],
     Operands<TM, TN>& cur, HalfFrags<TM>& fa, HalfFrags<TN>& fb,
-    const PipeLoader<TM * 64, NW>& la, const PipeLoader<TN * 64, NW>& lb,
+    const PipeLoader<BM, NW>& la, const PipeLoader<BN, NW>& lb,
     const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
     const uint8_t* b_scales, int arow, int brow, int lane, int wave) {
   constexpr int next = U == NS - 1 ? 0 : U + 1;
   constexpr int fill_slot = U == 0 ? NS - 1 : U - 1;   // stage kt - 1's slot
-  const bool fill = kt + NS - 1 < nk;
-  if (fill) {
-    const int64_t k0 = static_cast<int64_t>(kt + NS - 1) * kBK;
-    la.issue(a_codes, a_scales, k0, ring.a[fill_slot], ring.sa[fill_slot], wave);
-    lb.issue(b_codes, b_scales, k0, ring.b[fill_slot], ring.sb[fill_slot], wave);
+  constexpr int kIssues = PipeLoader<BM, NW>::kIssues + PipeLoader<BN, NW>::kIssues;
+  // Every stage issues the same loads, so the wait below is one count.  Past
+  // the last stage the fill repeats stage nk - 1 into the slot just freed,
+  // which no later stage reads.
+  {
+    const int fs = kt + NS - 1 < nk ? kt + NS - 1 : nk - 1;
+    const int64_t k0 = static_cast<int64_t>(fs) * kBK;
+    la.issue(k0, ring.a[fill_slot], ring.sa[fill_slot], wave);
+    lb.issue(k0, ring.b[fill_slot], ring.sb[fill_slot], wave);
   }
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
@@ -565,18 +595,22 @@ __device__ __forceinline__ void pipe_stage(
       else
         decode_step(nxt, na, nb, 0);
       mfma_step(acc, cur);
-      interleave_hint<TM * TN>();
+      // the stage's loads spread over the first k-step's MFMAs
+      if (half == 0 && j == 0)
+        interleave_hint<TM * TN, kIssues>();
+      else
+        interleave_hint<TM * TN, 0>();
+      // one scheduling region per k-step: the next half's fragments are
+      // consumed only by the last step's decode, so their LDS wait stays there
+      __builtin_amdgcn_sched_barrier(0);
       cur = nxt;
     }
     fa = na;
     fb = nb;
   }
-  // stage kt + 1 must have landed before the barrier; the fill just issued
-  // for stage kt + NS - 1 may stay in flight (NS > 3)
-  if (NS > 3 && fill)
-    __builtin_amdgcn_s_waitcnt(PipeLoader<TM * 64, NW>::kVmcntKeep);
-  else
-    __builtin_amdgcn_s_waitcnt(0);
+  // stage kt + 1 must have landed before the barrier; the fills of stages
+  // kt + 2 .. kt + NS - 1 may stay in flight
+  __builtin_amdgcn_s_waitcnt(kVmcntKeepOf((NS - 2) * kIssues));
   stage_barrier();
 }
 
@@ -594,27 +628,19 @@ w4a4_gemm_pipelined(const uint8_t* __restrict__ a_codes,
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   constexpr int NS = PIPE_STAGES;
   static_assert(NS >= 3 && NS <= 4, "ring depth");
-  static_assert(BM == TM * 64 && BN == TN * 64, "2 x 2 waves");
-  __shared__ __attribute__((aligned(1024))) uint8_t a0[BM * kPipeRowBytes], a1[BM * kPipeRowBytes],
-      a2[BM * kPipeRowBytes], a3[NS > 3 ? BM * kPipeRowBytes : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t b0[BN * kPipeRowBytes], b1[BN * kPipeRowBytes],
-      b2[BN * kPipeRowBytes], b3[NS > 3 ? BN * kPipeRowBytes : 16];
-  __shared__ __attribute__((aligned(256))) uint8_t sa0[BM * kPipeScaleBytes], sa1[BM * kPipeScaleBytes],
-      sa2[BM * kPipeScaleBytes], sa3[NS > 3 ? BM * kPipeScaleBytes : 16];
-  __shared__ __attribute__((aligned(256))) uint8_t sb0[BN * kPipeScaleBytes], sb1[BN * kPipeScaleBytes],
-      sb2[BN * kPipeScaleBytes], sb3[NS > 3 ? BN * kPipeScaleBytes : 16];
+  // one LDS object per slot (A codes, B codes, A scales, B scales)
+  constexpr int kSlotBytes = (BM + BN) * (kPipeRowBytes + kPipeScaleBytes);
+  __shared__ __attribute__((aligned(1024))) uint8_t s0[kSlotBytes], s1[kSlotBytes],
+      s2[kSlotBytes], s3[NS > 3 ? kSlotBytes : 16];
   Ring<NS> ring;
   {
-    uint8_t* const as[4] = {a0, a1, a2, a3};
-    uint8_t* const bs[4] = {b0, b1, b2, b3};
-    uint8_t* const sas[4] = {sa0, sa1, sa2, sa3};
-    uint8_t* const sbs[4] = {sb0, sb1, sb2, sb3};
+    uint8_t* const slots[4] = {s0, s1, s2, s3};
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      ring.a[i] = as[i];
-      ring.b[i] = bs[i];
-      ring.sa[i] = sas[i];
-      ring.sb[i] = sbs[i];
+      ring.a[i] = slots[i];
+      ring.b[i] = slots[i] + BM * kPipeRowBytes;
+      ring.sa[i] = slots[i] + (BM + BN) * kPipeRowBytes;
+      ring.sb[i] = slots[i] + (BM + BN) * kPipeRowBytes + BM * kPipeScaleBytes;
     }
   }
 
@@ -645,17 +671,22 @@ w4a4_gemm_pipelined(const uint8_t* __restrict__ a_codes,
   const int nk = static_cast<int>(k / kBK);
   PipeLoader<BM, NW> la;
   PipeLoader<BN, NW> lb;
-  la.init(m0, m, k, wave, lane);
-  lb.init(n0, n, k, wave, lane);
+  la.init(a_codes, a_scales, m0, m, k, wave, lane);
+  lb.init(b_codes, b_scales, n0, n, k, wave, lane);
   // prologue: stages 0 .. NS-2 into slots 0 .. NS-2
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st) {
     if (st < nk) {
-      la.issue(a_codes, a_scales, static_cast<int64_t>(st) * kBK, ring.a[st], ring.sa[st], wave);
-      lb.issue(b_codes, b_scales, static_cast<int64_t>(st) * kBK, ring.b[st], ring.sb[st], wave);
+      la.issue(static_cast<int64_t>(st) * kBK, ring.a[st], ring.sa[st], wave);
+      lb.issue(static_cast<int64_t>(st) * kBK, ring.b[st], ring.sb[st], wave);
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);   // all of this lane's loads have landed
+  // stage 0 must have landed; stages 1 .. NS-2 may stay in flight
+  constexpr int kIssues = PipeLoader<BM, NW>::kIssues + PipeLoader<BN, NW>::kIssues;
+  if (nk >= NS - 1)
+    __builtin_amdgcn_s_waitcnt(kVmcntKeepOf((NS - 2) * kIssues));
+  else
+    __builtin_amdgcn_s_waitcnt(0);
   stage_barrier();
 
   HalfFrags<TM> fa;
@@ -670,7 +701,7 @@ w4a4_gemm_pipelined(const uint8_t* __restrict__ a_codes,
   for (int kt0 = 0; kt0 < nk; kt0 += NS) {
 #define NVFP4_PIPE_STAGE(U)                                                    \
     if (kt0 + U < nk)                                                          \
-      pipe_stage<U, NS, TM, TN, NW>(ring, kt0 + U, nk, acc, cur, fa, fb, la, lb, \
+      pipe_stage<U, NS, TM, TN, NW, BM, BN>(ring, kt0 + U, nk, acc, cur, fa, fb, la, lb, \
                                     a_codes, a_scales, b_codes, b_scales,      \
                                     arow, brow, lane, wave);
     NVFP4_PIPE_STAGE(0)
@@ -679,6 +710,8 @@ w4a4_gemm_pipelined(const uint8_t* __restrict__ a_codes,
     if constexpr (NS > 3) { NVFP4_PIPE_STAGE(3) }
 #undef NVFP4_PIPE_STAGE
   }
+  // no fill may still be writing LDS when the workgroup ends
+  __builtin_amdgcn_s_waitcnt(0);
 
   const double gab = static_cast<double>(*a_global) * static_cast<double>(*b_global);
   const int col_l = lane & 31, row_l = (lane >> 5) * 4;
@@ -913,7 +946,8 @@ hipError_t dispatch_shape(const uint8_t* a_codes, const uint8_t* a_scales,
     if (m <= 64) return launch_skinny<2, 1, OUT, EPI>(NVFP4_ARGS);
     if (n <= 32) return launch_skinny<1, 1, OUT, EPI>(NVFP4_ARGS);
     if (n <= 64) return launch_skinny<1, 2, OUT, EPI>(NVFP4_ARGS);
-    return launch_pipelined<2, 2, 4, 4, OUT, EPI>(NVFP4_ARGS);
+    // the pipelined kernels address a tile with 32-bit offsets
+    if (k <= (int64_t{1} << 22)) return launch_pipelined<2, 2, 4, 4, OUT, EPI>(NVFP4_ARGS);
   }
   return launch_cfg<2, 2, 4, 4, ALIGNED, OUT, EPI>(NVFP4_ARGS);
 #undef NVFP4_ARGS

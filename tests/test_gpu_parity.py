@@ -314,7 +314,9 @@ def test_gemm_tiny_exact(out_dtype):
                                    (17, 300, 5136), (257, 513, 1024),
                                    (64, 64, 4096), (300, 20, 1024),
                                    (40, 1000, 512), (1000, 50, 256),
-                                   (7, 777, 384), (513, 257, 640)])
+                                   (7, 777, 384), (513, 257, 640),
+                                   (300, 200, 128), (130, 300, 256),
+                                   (200, 129, 384)])
 def test_gemm_ragged_shapes(m, n, k):
     rng = np.random.default_rng(m * 31 + n * 7 + k)
     xv = rng.standard_normal((m, k)).astype(np.float32)
