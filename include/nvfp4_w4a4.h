@@ -141,6 +141,9 @@ int nvfp4_harmonize_group(uint8_t* scales, int64_t k,
  *   b_codes, b_scales, b_global  weights B [n][k] (K-major, the same
  *                                layout; codes 16-byte aligned).
  *   m, n, k      m, n >= 1, k >= 16, k % 16 == 0.
+ *                Scale arrays may have any alignment; the fast kernels
+ *                need k % 128 == 0 and both scale arrays 16-byte aligned
+ *                (other calls take a slower kernel with byte-wise guards).
  *   out          device, [m][ldo] of out_dtype (F32 or BF16), ldo >= n;
  *                4-byte aligned.  Must not overlap the inputs.
  *   epilogue     w4a4_epilogue, applied in fp32 before the store.

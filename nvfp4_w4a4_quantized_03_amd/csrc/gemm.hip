@@ -85,7 +85,8 @@ __device__ __forceinline__ float epilogue(float y) {
 // Copies one operand's BK-wide stage (ROWS rows of codes and scales) from
 // global memory to LDS through registers.
 //
-// ALIGNED (k % 128 == 0, the shapes of the workloads): every 16-byte code
+// ALIGNED (k % 128 == 0 and 16-byte aligned scale arrays, as the
+// workloads have them): every 16-byte code
 // chunk and every row's 8 scale bytes of a stage lie inside k, so loads are
 // unconditional (rows past `rows` read a clamped, valid row) and row validity
 // is applied when storing to LDS.  No load result is consumed before the
@@ -753,36 +754,58 @@ hipError_t launch_pipelined(const uint8_t* a_codes, const uint8_t* a_scales,
 // ---------------------------------------------------------------------------
 // Skinny kernel: one operand has at most 64 rows (decode batches, the
 // per-head gate projections).  The other operand streams from HBM once, so
-// the shape is bandwidth-bound: there is no LDS staging; each lane loads
-// its own 16 code bytes (32 K of one row) and 2 block scales per 64-K chunk
-// straight into registers, several chunks in flight.  A workgroup owns one
-// TMT x TNT grid of 32 x 32 output tiles and its 4 waves split K; the
-// partial accumulators are summed through LDS before the epilogue.  Rows
+// the shape is bandwidth-bound: there is no LDS staging; operands go from
+// global memory straight into registers in the MFMA layout.  K is split
+// into groups of CPG 64-K chunks (CPG = 4, or 2 when k % 256 != 0); per
+// group and row a lane loads its 16 code bytes of each chunk (32 K, its
+// half of the chunk) and, in one load, the row's 4 * CPG block scales of
+// the whole group (loads touch one cache line per row, so fewer and wider
+// scale loads matter more than their bytes).  A workgroup owns one
+// TMT x TNT grid of 32 x 32 output tiles; its NWV waves take interleaved
+// groups, KG of them in flight per wave, and their partial accumulators
+// are summed through LDS, one tile at a time, before the epilogue.  Rows
 // past m or n read a clamped valid row and are never stored.
-// Requires k % 64 == 0.
+// Requires k % (64 * CPG) == 0.
 
-constexpr int kSkinnyWaves = 4;
-constexpr int kSkinnyUnroll = 4;   // 64-K chunks in flight per lane
+template <int CPG>
+struct SkinnyScales;
+template <>
+struct SkinnyScales<4> { using type = uint4; };
+template <>
+struct SkinnyScales<2> { using type = uint2; };
 
-struct ChunkFrag {
-  uint4 code;        // 32 K of one row (this lane's half of a 64-K chunk)
-  unsigned short sc; // its two E4M3 block scales
+template <int CPG>
+struct GroupFrag {
+  uint4 code[CPG];                          // 32 K of one row per chunk
+  typename SkinnyScales<CPG>::type sc;      // the row's 4 * CPG block scales
 };
 
-__device__ __forceinline__ ChunkFrag load_chunk(const uint8_t* __restrict__ codes,
-                                                const uint8_t* __restrict__ scales,
-                                                int64_t row, int64_t kbytes,
-                                                int64_t kblocks, int64_t chunk,
-                                                int h) {
-  ChunkFrag f;
-  f.code = *reinterpret_cast<const uint4*>(codes + row * kbytes + chunk * 32 + h * 16);
-  f.sc = *reinterpret_cast<const unsigned short*>(scales + row * kblocks + chunk * 4 + h * 2);
-  return f;
+template <int CPG>
+__device__ __forceinline__ void load_group(GroupFrag<CPG>& f, const uint8_t* __restrict__ codes,
+                                           const uint8_t* __restrict__ scales,
+                                           int64_t row, int64_t kbytes, int64_t kblocks,
+                                           int64_t group, int h) {
+  const uint8_t* c = codes + row * kbytes + group * (CPG * 32) + h * 16;
+#pragma unroll
+  for (int q = 0; q < CPG; ++q) f.code[q] = *reinterpret_cast<const uint4*>(c + q * 32);
+  f.sc = *reinterpret_cast<const typename SkinnyScales<CPG>::type*>(
+      scales + row * kblocks + group * (CPG * 4));
 }
 
-// operand of k-step j (0..3) of a chunk: codes dword j, block j / 2
-__device__ __forceinline__ half8_t chunk_operand(const ChunkFrag& f, unsigned sc2, int j) {
-  const unsigned w = j == 0 ? f.code.x : j == 1 ? f.code.y : j == 2 ? f.code.z : f.code.w;
+// the two E4M3 scales of chunk q's half h (low byte = first block)
+template <int CPG>
+__device__ __forceinline__ unsigned group_scale_pair(const GroupFrag<CPG>& f, int q, int h) {
+  unsigned w;
+  if constexpr (CPG == 4)
+    w = q == 0 ? f.sc.x : q == 1 ? f.sc.y : q == 2 ? f.sc.z : f.sc.w;
+  else
+    w = q == 0 ? f.sc.x : f.sc.y;
+  return h ? w >> 16 : w & 0xFFFFu;
+}
+
+// operand of k-step j (0..3) of one chunk: codes dword j, block j / 2
+__device__ __forceinline__ half8_t chunk_operand(const uint4& code, unsigned sc2, int j) {
+  const unsigned w = j == 0 ? code.x : j == 1 ? code.y : j == 2 ? code.z : code.w;
   const unsigned short sb = (j >> 1) ? static_cast<unsigned short>(sc2 >> 16)
                                      : static_cast<unsigned short>(sc2 & 0xFFFFu);
   const _Float16 sv = __builtin_bit_cast(_Float16, sb);
@@ -792,8 +815,8 @@ __device__ __forceinline__ half8_t chunk_operand(const ChunkFrag& f, unsigned sc
   return decode8(w, s);
 }
 
-template <int TMT, int TNT, int OUT, int EPI>
-__global__ void __launch_bounds__(kSkinnyWaves * 64)
+template <int TMT, int TNT, int NWV, int KG, int CPG, int OUT, int EPI>
+__global__ void __launch_bounds__(NWV * 64)
 w4a4_gemm_skinny(const uint8_t* __restrict__ a_codes,
                  const uint8_t* __restrict__ a_scales,
                  const float* __restrict__ a_global, int64_t m,
@@ -806,7 +829,7 @@ w4a4_gemm_skinny(const uint8_t* __restrict__ a_codes,
   const int64_t m0 = static_cast<int64_t>(blockIdx.x / tiles_n) * (32 * TMT);
   const int64_t n0 = static_cast<int64_t>(blockIdx.x % tiles_n) * (32 * TNT);
   const int64_t kbytes = k / 2, kblocks = k / 16;
-  const int64_t nchunks = k / 64;
+  const int64_t ngroups = k / (64 * CPG);
 
   int64_t arow[TMT], brow[TNT];
 #pragma unroll
@@ -828,80 +851,85 @@ w4a4_gemm_skinny(const uint8_t* __restrict__ a_codes,
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // wave w takes chunks w, w + 4, w + 8, ...
-  for (int64_t c0 = wave; c0 < nchunks; c0 += kSkinnyWaves * kSkinnyUnroll) {
-    ChunkFrag fa[kSkinnyUnroll][TMT], fb[kSkinnyUnroll][TNT];
+  // wave w takes groups w, w + NWV, w + 2 NWV, ...
+  for (int64_t g0 = wave; g0 < ngroups; g0 += NWV * KG) {
+    GroupFrag<CPG> fa[KG][TMT], fb[KG][TNT];
 #pragma unroll
-    for (int u = 0; u < kSkinnyUnroll; ++u) {
-      const int64_t c = c0 + u * kSkinnyWaves;
-      const int64_t cc = c < nchunks ? c : nchunks - 1;   // clamped, unused
+    for (int u = 0; u < KG; ++u) {
+      const int64_t g = g0 + u * NWV;
+      const int64_t gg = g < ngroups ? g : ngroups - 1;   // clamped, unused
 #pragma unroll
-      for (int i = 0; i < TMT; ++i) fa[u][i] = load_chunk(a_codes, a_scales, arow[i], kbytes, kblocks, cc, h);
+      for (int i = 0; i < TMT; ++i) load_group(fa[u][i], a_codes, a_scales, arow[i], kbytes, kblocks, gg, h);
 #pragma unroll
-      for (int j = 0; j < TNT; ++j) fb[u][j] = load_chunk(b_codes, b_scales, brow[j], kbytes, kblocks, cc, h);
+      for (int j = 0; j < TNT; ++j) load_group(fb[u][j], b_codes, b_scales, brow[j], kbytes, kblocks, gg, h);
     }
-    // every chunk is computed; a chunk past k (clamped load) gets block
+    // every group is computed; a group past k (clamped load) gets block
     // scale 0, so all its products are exactly 0
 #pragma unroll
-    for (int u = 0; u < kSkinnyUnroll; ++u) {
-      const bool valid = c0 + u * kSkinnyWaves < nchunks;
-      unsigned sa[TMT], sb[TNT];
+    for (int u = 0; u < KG; ++u) {
+      const bool valid = g0 + u * NWV < ngroups;
 #pragma unroll
-      for (int i = 0; i < TMT; ++i)
-        sa[i] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
-                    valid ? fa[u][i].sc : 0u, 1.0f, false));
-#pragma unroll
-      for (int j = 0; j < TNT; ++j)
-        sb[j] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
-                    valid ? fb[u][j].sc : 0u, 1.0f, false));
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        half8_t av[TMT], bv[TNT];
-#pragma unroll
-        for (int i = 0; i < TMT; ++i) av[i] = chunk_operand(fa[u][i], sa[i], ks);
-#pragma unroll
-        for (int j = 0; j < TNT; ++j) bv[j] = chunk_operand(fb[u][j], sb[j], ks);
+      for (int q = 0; q < CPG; ++q) {
+        unsigned sa[TMT], sb[TNT];
 #pragma unroll
         for (int i = 0; i < TMT; ++i)
+          sa[i] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+                      valid ? group_scale_pair(fa[u][i], q, h) : 0u, 1.0f, false));
 #pragma unroll
-          for (int j = 0; j < TNT; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < TNT; ++j)
+          sb[j] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+                      valid ? group_scale_pair(fb[u][j], q, h) : 0u, 1.0f, false));
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          half8_t av[TMT], bv[TNT];
+#pragma unroll
+          for (int i = 0; i < TMT; ++i) av[i] = chunk_operand(fa[u][i].code[q], sa[i], ks);
+#pragma unroll
+          for (int j = 0; j < TNT; ++j) bv[j] = chunk_operand(fb[u][j].code[q], sb[j], ks);
+#pragma unroll
+          for (int i = 0; i < TMT; ++i)
+#pragma unroll
+            for (int j = 0; j < TNT; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        }
       }
     }
   }
 
-  // sum the waves' partial accumulators: red[wave][tile][e][lane]
-  __shared__ float red[kSkinnyWaves][TMT * TNT][16][64];
-#pragma unroll
-  for (int i = 0; i < TMT; ++i)
-#pragma unroll
-    for (int j = 0; j < TNT; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) red[wave][i * TNT + j][e][lane] = acc[i][j][e];
-  __syncthreads();
+  // sum the waves' partial accumulators, one 32 x 32 tile at a time:
+  // red[wave][e][lane]
+  __shared__ float red[NWV][16][64];
   const double gab = static_cast<double>(*a_global) * static_cast<double>(*b_global);
-  constexpr int kVals = TMT * TNT * 16 * 64;
 #pragma unroll
-  for (int v0 = 0; v0 < kVals; v0 += kSkinnyWaves * 64) {
-    const int v = v0 + threadIdx.x;
-    const int l = v & 63, e = (v >> 6) & 15, t = v >> 10;
-    float sum = red[0][t][e][l];
-#pragma unroll
-    for (int w = 1; w < kSkinnyWaves; ++w) sum += red[w][t][e][l];
+  for (int t = 0; t < TMT * TNT; ++t) {
     const int ti = t / TNT, tj = t % TNT;
-    const int64_t row = m0 + ti * 32 + 8 * (e >> 2) + (l >> 5) * 4 + (e & 3);
-    const int64_t col = n0 + tj * 32 + (l & 31);
-    if (row < m && col < n) {
-      const float y = epilogue<EPI>(static_cast<float>(static_cast<double>(sum) * gab));
-      if constexpr (OUT == kOutF32)
-        static_cast<float*>(out)[row * ldo + col] = y;
-      else
-        static_cast<unsigned short*>(out)[row * ldo + col] = f32_to_bf16_rne(y);
+    if (t > 0) __syncthreads();   // the previous tile's sums are read
+#pragma unroll
+    for (int e = 0; e < 16; ++e) red[wave][e][lane] = acc[ti][tj][e];
+    __syncthreads();
+#pragma unroll
+    for (int v0 = 0; v0 < 16 * 64; v0 += NWV * 64) {
+      const int v = v0 + threadIdx.x;
+      if (NWV * 64 <= 16 * 64 || v < 16 * 64) {
+        const int l = v & 63, e = v >> 6;
+        float sum = red[0][e][l];
+#pragma unroll
+        for (int w = 1; w < NWV; ++w) sum += red[w][e][l];
+        const int64_t row = m0 + ti * 32 + 8 * (e >> 2) + (l >> 5) * 4 + (e & 3);
+        const int64_t col = n0 + tj * 32 + (l & 31);
+        if (row < m && col < n) {
+          const float y = epilogue<EPI>(static_cast<float>(static_cast<double>(sum) * gab));
+          if constexpr (OUT == kOutF32)
+            static_cast<float*>(out)[row * ldo + col] = y;
+          else
+            static_cast<unsigned short*>(out)[row * ldo + col] = f32_to_bf16_rne(y);
+        }
+      }
     }
   }
 }
 
-template <int TMT, int TNT, int OUT, int EPI>
+template <int TMT, int TNT, int NWV, int KG, int OUT, int EPI>
 hipError_t launch_skinny(const uint8_t* a_codes, const uint8_t* a_scales,
                          const float* a_global, int64_t m,
                          const uint8_t* b_codes, const uint8_t* b_scales,
@@ -909,10 +937,15 @@ hipError_t launch_skinny(const uint8_t* a_codes, const uint8_t* a_scales,
                          void* out, int64_t ldo, hipStream_t stream) {
   const int64_t tm = (m + 32 * TMT - 1) / (32 * TMT), tn = (n + 32 * TNT - 1) / (32 * TNT);
   if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
-  w4a4_gemm_skinny<TMT, TNT, OUT, EPI>
-      <<<static_cast<unsigned>(tm * tn), kSkinnyWaves * 64, 0, stream>>>(
-          a_codes, a_scales, a_global, m, b_codes, b_scales, b_global, n, k,
-          out, ldo, static_cast<int>(tn));
+  const unsigned grid = static_cast<unsigned>(tm * tn);
+  if (k % 256 == 0)
+    w4a4_gemm_skinny<TMT, TNT, NWV, KG, 4, OUT, EPI><<<grid, NWV * 64, 0, stream>>>(
+        a_codes, a_scales, a_global, m, b_codes, b_scales, b_global, n, k, out, ldo,
+        static_cast<int>(tn));
+  else
+    w4a4_gemm_skinny<TMT, TNT, NWV, 2 * KG, 2, OUT, EPI><<<grid, NWV * 64, 0, stream>>>(
+        a_codes, a_scales, a_global, m, b_codes, b_scales, b_global, n, k, out, ldo,
+        static_cast<int>(tn));
   return hipGetLastError();
 }
 
@@ -941,11 +974,12 @@ hipError_t dispatch_shape(const uint8_t* a_codes, const uint8_t* a_scales,
 #define NVFP4_ARGS a_codes, a_scales, a_global, m, b_codes, b_scales, b_global, \
                    n, k, out, ldo, stream
   if constexpr (ALIGNED) {
-    // k % 128 == 0 here, so the skinny kernel's 64-K chunks tile k
-    if (m <= 32) return launch_skinny<1, 1, OUT, EPI>(NVFP4_ARGS);
-    if (m <= 64) return launch_skinny<2, 1, OUT, EPI>(NVFP4_ARGS);
-    if (n <= 32) return launch_skinny<1, 1, OUT, EPI>(NVFP4_ARGS);
-    if (n <= 64) return launch_skinny<1, 2, OUT, EPI>(NVFP4_ARGS);
+    // k % 128 == 0 here, so the skinny kernel's groups of 2 or 4 64-K
+    // chunks tile k
+    if (m <= 32) return launch_skinny<1, 1, 4, 1, OUT, EPI>(NVFP4_ARGS);
+    if (m <= 64) return launch_skinny<2, 1, 4, 1, OUT, EPI>(NVFP4_ARGS);
+    if (n <= 32) return launch_skinny<1, 1, 4, 1, OUT, EPI>(NVFP4_ARGS);
+    if (n <= 64) return launch_skinny<2, 2, 4, 1, OUT, EPI>(NVFP4_ARGS);
     // the pipelined kernels address a tile with 32-bit offsets
     if (k <= (int64_t{1} << 22)) return launch_pipelined<2, 2, 4, 4, OUT, EPI>(NVFP4_ARGS);
   }
@@ -959,9 +993,12 @@ hipError_t dispatch_align(const uint8_t* a_codes, const uint8_t* a_scales,
                           const uint8_t* b_codes, const uint8_t* b_scales,
                           const float* b_global, int64_t n, int64_t k,
                           void* out, int64_t ldo, hipStream_t stream) {
-  // whole stages (k % 128 == 0): unconditional 16-byte code loads and
-  // 8-byte scale loads
-  const bool aligned = k % kBK == 0;
+  // whole stages (k % 128 == 0) and 16-byte aligned scale arrays:
+  // unconditional 16-byte code loads and wide (8- or 16-byte) scale loads;
+  // anything else takes the guarded, byte-wise scale path
+  const bool aligned = k % kBK == 0 &&
+                       reinterpret_cast<uintptr_t>(a_scales) % 16 == 0 &&
+                       reinterpret_cast<uintptr_t>(b_scales) % 16 == 0;
   if (aligned)
     return dispatch_shape<true, OUT, EPI>(a_codes, a_scales, a_global, m,
                                           b_codes, b_scales, b_global, n, k,

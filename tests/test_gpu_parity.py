@@ -316,7 +316,7 @@ def test_gemm_tiny_exact(out_dtype):
                                    (40, 1000, 512), (1000, 50, 256),
                                    (7, 777, 384), (513, 257, 640),
                                    (300, 200, 128), (130, 300, 256),
-                                   (200, 129, 384)])
+                                   (200, 129, 384), (33, 700, 640)])
 def test_gemm_ragged_shapes(m, n, k):
     rng = np.random.default_rng(m * 31 + n * 7 + k)
     xv = rng.standard_normal((m, k)).astype(np.float32)
@@ -332,6 +332,31 @@ def test_gemm_ragged_shapes(m, n, k):
     assert rel_frob(ya.astype(np.float64), oracle.gate_alpha(ref)) <= TOL
     yb = host(nv.gemm(qa, qb, out_dtype=torch.float32, epilogue="beta"))
     assert rel_frob(yb.astype(np.float64), oracle.gate_beta(ref)) <= TOL
+
+
+@pytest.mark.parametrize("m,n,k", [(32, 300, 512), (300, 40, 256),
+                                   (200, 300, 384)])
+def test_gemm_unaligned_scale_arrays(m, n, k):
+    """Scale arrays at an odd byte offset take the guarded kernel and give
+    the same result as the oracle (the ABI puts no alignment on scales)."""
+    rng = np.random.default_rng(m + 3 * n + k)
+    xv = rng.standard_normal((m, k)).astype(np.float32)
+    wv = (rng.standard_normal((n, k)) * 0.05).astype(np.float32)
+    _say("gemm unaligned scales", m, n, k)
+    qa = nv.quantize(up(xv, None, "f32"))
+    qb = nv.quantize(up(wv, None, "f32"))
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=torch.uint8, device=DEV)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        assert v.data_ptr() % 2 == 1
+        return v
+    qa2 = nv.NVFP4(qa.codes, shifted(qa.scales), qa.global_scale)
+    qb2 = nv.NVFP4(qb.codes, shifted(qb.scales), qb.global_scale)
+    ref = oracle.gemm_exact_int(*oracle.quantize(xv), *oracle.quantize(wv))
+    y = host(nv.gemm(qa2, qb2, out_dtype=torch.float32)).astype(np.float64)
+    assert rel_frob(y, ref) <= TOL
 
 
 def test_gemm_strided_output():
