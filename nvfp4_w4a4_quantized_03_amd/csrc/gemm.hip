@@ -714,6 +714,9 @@ w4a4_gemm_pipelined(const uint8_t* __restrict__ a_codes,
   // no fill may still be writing LDS when the workgroup ends
   __builtin_amdgcn_s_waitcnt(0);
 
+  // the output (often larger than the memory-side cache) is streamed out
+  // with non-temporal stores, so that it does not linger there as dirty
+  // lines for the next kernel to write back
   const double gab = static_cast<double>(*a_global) * static_cast<double>(*b_global);
   const int col_l = lane & 31, row_l = (lane >> 5) * 4;
 #pragma unroll
@@ -727,9 +730,9 @@ w4a4_gemm_pipelined(const uint8_t* __restrict__ a_codes,
         if (row < m && col < n) {
           const float y = epilogue<EPI>(static_cast<float>(static_cast<double>(acc[i][j][e]) * gab));
           if constexpr (OUT == kOutF32)
-            static_cast<float*>(out)[row * ldo + col] = y;
+            __builtin_nontemporal_store(y, static_cast<float*>(out) + row * ldo + col);
           else
-            static_cast<unsigned short*>(out)[row * ldo + col] = f32_to_bf16_rne(y);
+            __builtin_nontemporal_store(f32_to_bf16_rne(y), static_cast<unsigned short*>(out) + row * ldo + col);
         }
       }
     }

@@ -239,10 +239,29 @@ __device__ __forceinline__ const uint8_t* block_src(const uint8_t* x, int64_t b,
   return x + row * ldx_bytes + (b - row * kb) * kBlockBytes;
 }
 
+// One block: load, encode, store.
+template <int DTYPE>
+__device__ __forceinline__ void quantize_one(const uint8_t* __restrict__ src, int64_t b,
+                                             float g, float inv6g, bool g_ok,
+                                             uint8_t* __restrict__ codes,
+                                             uint8_t* __restrict__ scales, float* row) {
+  RawBlock<DTYPE> raw;
+  fetch_block<DTYPE>(src, raw);
+  float v[16];
+  const float m = __uint_as_float(unpack_block(raw, v));
+  unsigned sc;
+  uint2 cc;
+  encode_block(v, m, g, inv6g, g_ok, &sc, &cc, row);
+  __builtin_nontemporal_store(cc.x, reinterpret_cast<unsigned*>(codes) + 2 * b);
+  __builtin_nontemporal_store(cc.y, reinterpret_cast<unsigned*>(codes) + 2 * b + 1);
+  __builtin_nontemporal_store(static_cast<uint8_t>(sc), scales + b);
+}
+
 // One block per lane: a wave's loads cover 64 consecutive blocks (2 KiB of
 // bf16).  Many short-lived waves per CU overlap the loads of some with the
-// encoding work of others; the grid-stride loop only matters for grids
-// larger than the launch limit.
+// encoding work of others.  A grid that covers every block (the launcher's
+// normal case) takes a straight-line body; the grid-stride loop only serves
+// grids capped at the launch limit.
 template <int DTYPE>
 __global__ void __launch_bounds__(256)
 quantize_kernel(const uint8_t* __restrict__ x, int64_t nblocks, int64_t kb,
@@ -258,18 +277,15 @@ quantize_kernel(const uint8_t* __restrict__ x, int64_t nblocks, int64_t kb,
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   __shared__ __attribute__((aligned(16))) float lds_rows[256 * kRowFloats];
   float* row = lds_rows + threadIdx.x * kRowFloats;
-  for (int64_t b = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-       b < nblocks; b += stride) {
-    RawBlock<DTYPE> raw;
-    fetch_block<DTYPE>(block_src<DTYPE>(x, b, contiguous, kb, ldx_bytes), raw);
-    float v[16];
-    const float m = __uint_as_float(unpack_block(raw, v));
-    unsigned sc;
-    uint2 cc;
-    encode_block(v, m, g, inv6g, g_ok, &sc, &cc, row);
-    reinterpret_cast<uint2*>(codes)[b] = cc;
-    scales[b] = static_cast<uint8_t>(sc);
+  const int64_t b0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (stride >= nblocks && contiguous) {
+    if (b0 < nblocks)
+      quantize_one<DTYPE>(x + b0 * (16 * kElemBytes), b0, g, inv6g, g_ok, codes, scales, row);
+    return;
   }
+  for (int64_t b = b0; b < nblocks; b += stride)
+    quantize_one<DTYPE>(block_src<DTYPE>(x, b, contiguous, kb, ldx_bytes), b, g, inv6g,
+                        g_ok, codes, scales, row);
 }
 
 // ---- self-calibrated global: amax over the tensor, then g = amax / 2688 --
