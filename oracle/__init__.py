@@ -29,7 +29,8 @@ from .formats import (E2M1_MAG, e2m1_decode, e4m3_decode, e4m3_decode_table,
                       bf16_rne_from_f64, GLOBAL_DIVISOR)
 from .quantize import (quantize, quantize_exact, dequantize, global_scale,
                        block_scales, encode_elements,
-                       unpack_codes, pack_codes)
+                       unpack_codes, pack_codes, dequantize_f32,
+                       dequantize_bf16, error_stats)
 from .harmonize import harmonize, harmonize_exact
 from .gemm import (gemm_exact_int, gemm_f64, gemm_f64_rows_cols, gate_alpha,
                    gate_beta, decoded_units)
@@ -40,6 +41,7 @@ __all__ = [
     "bf16_rne_from_f64", "GLOBAL_DIVISOR",
     "quantize", "quantize_exact", "dequantize", "global_scale",
     "unpack_codes", "pack_codes", "block_scales", "encode_elements",
+    "dequantize_f32", "dequantize_bf16", "error_stats",
     "harmonize", "harmonize_exact",
     "gemm_exact_int", "gemm_f64", "gemm_f64_rows_cols", "gate_alpha",
     "gate_beta", "decoded_units",

@@ -37,7 +37,7 @@ import numpy as np
 
 from .formats import (E2M1_MAG, GLOBAL_DIVISOR, e2m1_rne_sat_exact,
                       e4m3_decode, e4m3_rne_sat_exact, fp32_rne_exact,
-                      e4m3_decode_table)
+                      e4m3_decode_table, bf16_rne_from_f64)
 
 BLOCK = 16
 
@@ -145,6 +145,32 @@ def dequantize(codes, scales, g):
     sc = e4m3_decode_table()[np.asarray(scales, dtype=np.int64)]
     sc = np.repeat(sc, BLOCK, axis=1)
     return sgn * mag * sc * float(g)
+
+
+def dequantize_f32(codes, scales, g):
+    """binary32 output of the dequantiser: each exact value sign * E2M1 *
+    E4M3 * g rounded once to nearest even (numpy's float64 -> float32 cast
+    is that rounding; the float64 value is exact, <= 30 significant bits)."""
+    return dequantize(codes, scales, g).astype(np.float32)
+
+
+def dequantize_bf16(codes, scales, g):
+    """bfloat16 output of the dequantiser: each exact value rounded once to
+    nearest even bfloat16.  Returns the uint16 bit patterns."""
+    return bf16_rne_from_f64(dequantize(codes, scales, g))[1]
+
+
+def error_stats(x, codes, scales, g):
+    """Per-row sums behind the A4 / W4 error percentages and the max/RMS
+    statistic ([P1] 접근 방법, the input statistics of Table 2; [P3] 前提1
+    for max/RMS): float64 [rows, 3] = (sum x^2, sum (x - x_hat)^2, max |x|)
+    with x_hat the exact dequantised value.  Relative error of a row or a
+    tensor = sqrt(sum of column 1 / sum of column 0); max/RMS of a row =
+    column 2 / sqrt(column 0 / K)."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x - dequantize(codes, scales, g)
+    return np.stack([np.sum(x * x, axis=1), np.sum(d * d, axis=1),
+                     np.max(np.abs(x), axis=1)], axis=1)
 
 
 def quantize_exact(x, g=None):

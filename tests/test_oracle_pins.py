@@ -506,3 +506,89 @@ def test_sanity_band_of_round_trip_error():
     q = oracle.quantize(x)
     err = np.linalg.norm(oracle.dequantize(*q) - x) / np.linalg.norm(x)
     assert 0.03 < err < 0.15
+
+
+# ------------------------------------------------- dequantise and error stats
+
+def _exact_values(codes, scales, g):
+    """Fraction value of every element, from the bit layouts alone."""
+    c = oracle.unpack_codes(codes)
+    out = []
+    for r in range(c.shape[0]):
+        row = []
+        for i in range(c.shape[1]):
+            code = int(c[r, i])
+            mag = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2),
+                   Fraction(2), Fraction(3), Fraction(4), Fraction(6)][code & 7]
+            sb = int(scales[r, i // 16])
+            e, mnt = sb >> 3, sb & 7
+            sc = (Fraction(mnt, 8) * Fraction(2) ** -6 if e == 0
+                  else (1 + Fraction(mnt, 8)) * Fraction(2) ** (e - 7))
+            row.append((-1 if code & 8 else 1) * mag * sc * Fraction(float(g)))
+        out.append(row)
+    return out
+
+
+def _bf16_rne_fraction(q):
+    """Nearest-even bfloat16 of a rational (8 significant bits, quantum
+    floor 2^-133), as a Fraction; written from the format, not the oracle."""
+    if q == 0:
+        return Fraction(0)
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    quantum = Fraction(2) ** max(e - 7, -133)
+    n = a / quantum
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return (1 if q > 0 else -1) * fl * quantum
+
+
+@pytest.mark.parametrize("g", [0.011, 2.0 ** -140, 3.0e-41, 1.25e30])
+def test_dequantize_roundings_against_fractions(g):
+    """binary32 and bfloat16 outputs are single roundings of the exact
+    products, including products in the subnormal range."""
+    rng = np.random.default_rng(17)
+    rows, k = 3, 64
+    codes = rng.integers(0, 256, size=(rows, k // 2)).astype(np.uint8)
+    scales = rng.integers(0, 0x7F, size=(rows, k // 16)).astype(np.uint8)
+    g = np.float32(g)
+    exact = _exact_values(codes, scales, g)
+    f32 = oracle.dequantize_f32(codes, scales, g)
+    b16 = oracle.dequantize_bf16(codes, scales, g)
+    for r in range(rows):
+        for i in range(k):
+            assert float(f32[r, i]) == oq.fp32_rne_exact(exact[r][i]) or \
+                (exact[r][i] == 0 and f32[r, i] == 0)
+            want = _bf16_rne_fraction(exact[r][i])
+            got = (np.uint32(b16[r, i]) << 16).view(np.float32)
+            assert Fraction(float(got)) == want
+
+
+def test_error_stats_against_fractions_and_invariants():
+    """Row sums equal their Fraction-exact values; values on the grid have
+    zero error; a one-hot row of one block has max/RMS exactly 4."""
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((4, 32)) * 3).astype(np.float32)
+    c, s, g = oracle.quantize(x)
+    st = oracle.error_stats(x, c, s, g)
+    xh = _exact_values(c, s, g)
+    for r in range(4):
+        xs = [Fraction(float(v)) for v in x[r]]
+        sx = sum(v * v for v in xs)
+        se = sum((v - w) ** 2 for v, w in zip(xs, xh[r]))
+        assert abs(Fraction(st[r, 0]) - sx) <= sx * Fraction(1, 2 ** 50)
+        assert abs(Fraction(st[r, 1]) - se) <= se * Fraction(1, 2 ** 40)
+        assert st[r, 2] == max(abs(float(v)) for v in x[r])
+    g2 = np.float32(2.0 ** -7)   # products exact in binary32
+    xg = oracle.dequantize(c, s, g2)
+    assert np.array_equal(xg.astype(np.float32).astype(np.float64), xg)
+    assert np.all(oracle.error_stats(xg.astype(np.float32), c, s, g2)[:, 1] == 0.0)
+    one = np.zeros((1, 16), dtype=np.float32)
+    one[0, 5] = -3.5
+    c1, s1, g1 = oracle.quantize(one)
+    st1 = oracle.error_stats(one, c1, s1, g1)
+    assert st1[0, 2] / np.sqrt(st1[0, 0] / 16) == 4.0
