@@ -132,7 +132,9 @@ def other_workloads(nv, synth, dev, stream, reps=10):
     """Kernel timings of the other workloads at hidden size 5120 (inputs
     resident in HBM): in_proj 4096x12288, gate projections 32768x64 with
     alpha/beta epilogues, a harmonised fused group (N = 17536), the tiny
-    16x128x256 case, and the self-calibrated (COMPUTE) activation quantize."""
+    16x128x256 case, the self-calibrated (COMPUTE) activation quantize, and
+    dequantisation to bf16 plus per-row error statistics of the 32768x5120
+    activations."""
     import numpy as np
     import torch
 
@@ -208,6 +210,18 @@ def other_workloads(nv, synth, dev, stream, reps=10):
     t_c = _time(lambda: nv.quantize(xv, out=(q.codes, q.scales)), reps, stream)
     out["quantize_compute_32768x5120"] = {
         "us": t_c, "gbps_4.5625B_per_elem": 32768 * 5120 * 4.5625 / t_c / 1e3}
+    # dequantise (fake-quant half) to bf16 and per-row error statistics
+    yb = torch.empty((32768, 5120), dtype=torch.bfloat16, device=dev)
+    t_d = _time(lambda: nv.dequantize(q, torch.bfloat16, out=yb), reps, stream)
+    t_e = _time(lambda: nv.error_stats(xv, q), reps, stream)
+    elems = 32768 * 5120
+    out["dequantize_error_stats_32768x5120"] = {
+        "dequantize_bf16_us": t_d,
+        "dequantize_gbps_2.5625B_per_elem": elems * 2.5625 / t_d / 1e3,
+        "dequantize_frac_hbm_peak": elems * 2.5625 / t_d / 1e3 / PEAK_HBM_GBPS,
+        "error_stats_us": t_e,
+        "error_stats_gbps_2.5625B_per_elem": elems * 2.5625 / t_e / 1e3,
+        "error_stats_frac_hbm_peak": elems * 2.5625 / t_e / 1e3 / PEAK_HBM_GBPS}
     return out
 
 

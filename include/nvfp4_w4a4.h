@@ -160,6 +160,47 @@ int w4a4_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
               void* out, int out_dtype, int64_t ldo, int epilogue,
               void* stream);
 
+/*
+ * nvfp4_dequantize -- values of an NVFP4 tensor, the inverse map used for
+ * fake quantisation (quantise, then dequantise) in the mechanism study of
+ * [P1] 접근 방법; element value sign * E2M1 * E4M3 * g per [P3] 前提1.
+ *
+ *   codes, scales, global  a [rows][k] NVFP4 tensor in the layout above
+ *                          (codes 8-byte aligned; global one float).
+ *   rows, k      rows >= 1, k >= 16, k % 16 == 0.
+ *   out          device, out, [rows][ldo] of out_dtype (F32 or BF16),
+ *                ldo >= k; 16-byte aligned, ldo*size a multiple of 16.
+ *                Must not overlap the inputs.
+ *
+ * Result: each output is the exact value rounded once to nearest even
+ * binary32 or bfloat16 (e2m1 * e4m3 is exact; times g it has <= 30
+ * significant bits, so no double rounding occurs).
+ */
+int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
+                     const float* global, int64_t rows, int64_t k, void* out,
+                     int out_dtype, int64_t ldo, void* stream);
+
+/*
+ * nvfp4_error_stats -- per-row statistics of a tensor and of its NVFP4
+ * quantisation, behind the A4 / W4 error percentages and the max/RMS input
+ * statistic of [P1] 접근 방법 (Table 2) and the block bound of [P3] 前提1.
+ *
+ *   x            device, [rows][ldx] of x_dtype (F32 or BF16), the tensor
+ *                that was quantised (same alignment rules as
+ *                nvfp4_quantize).
+ *   codes, scales, global  its NVFP4 form (codes 8-byte aligned).
+ *   stats        device, out, [rows][3] doubles, 8-byte aligned:
+ *                sum x^2, sum (x - x_hat)^2, max |x| with x_hat the exact
+ *                dequantised value; sums in float64 in an unspecified
+ *                order.  Must not overlap the inputs.
+ *
+ * Relative error of a row or tensor = sqrt(sum col 1 / sum col 0);
+ * max/RMS of a row = col 2 / sqrt(col 0 / k).
+ */
+int nvfp4_error_stats(const void* x, int x_dtype, int64_t rows, int64_t k,
+                      int64_t ldx, const uint8_t* codes, const uint8_t* scales,
+                      const float* global, double* stats, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* nvfp4_status_string(int status);
 

@@ -17,7 +17,8 @@ from collections import namedtuple
 
 import torch
 
-__all__ = ["NVFP4", "quantize", "harmonize_group", "gemm", "library",
+__all__ = ["NVFP4", "quantize", "harmonize_group", "gemm", "dequantize",
+           "fake_quantize", "error_stats", "library",
            "LIB_PATH", "NVFP4Error"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
@@ -61,6 +62,11 @@ def library():
     L.w4a4_gemm.argtypes = [vp, vp, vp, i64, vp, vp, vp, i64, i64, vp, i32,
                             i64, i32, vp]
     L.w4a4_gemm.restype = i32
+    L.nvfp4_dequantize.argtypes = [vp, vp, vp, i64, i64, vp, i32, i64, vp]
+    L.nvfp4_dequantize.restype = i32
+    L.nvfp4_error_stats.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp,
+                                    vp]
+    L.nvfp4_error_stats.restype = i32
     L.nvfp4_status_string.argtypes = [i32]
     L.nvfp4_status_string.restype = ctypes.c_char_p
     L.nvfp4_abi_version.argtypes = []
@@ -202,3 +208,65 @@ def gemm(a, b, out_dtype=torch.bfloat16, epilogue="none", out=None):
                                EPILOGUES[epilogue],
                                _stream(ac)))
     return out
+
+
+def _nvfp4_parts(q, name):
+    codes, scales, g = q
+    for t, nm in ((codes, name + ".codes"), (scales, name + ".scales"),
+                  (g, name + ".global_scale")):
+        _device_tensor(t, nm)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % nm)
+    return codes, scales, g
+
+
+def dequantize(q, out_dtype=torch.bfloat16, out=None):
+    """Values of an NVFP4 tensor q ([rows, k]): sign * E2M1 * E4M3 * g,
+    each rounded once to out_dtype (float32 or bfloat16).  Returns a
+    [rows, k] GPU tensor (or fills out, which may be a row-strided view)."""
+    codes, scales, g = _nvfp4_parts(q, "q")
+    rows, k = codes.shape[0], codes.shape[1] * 2
+    od = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}.get(out_dtype)
+    if od is None:
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    if out is None:
+        out = torch.empty((rows, k), dtype=out_dtype, device=codes.device)
+    elif out.dtype != out_dtype or out.shape != (rows, k) or out.stride(1) != 1:
+        raise ValueError("out must be [rows, k] of out_dtype with unit column stride")
+    ldo = out.stride(0) if rows > 1 else k
+    _check(library().nvfp4_dequantize(_ptr(codes), _ptr(scales), _ptr(g), rows,
+                                      k, _ptr(out), od, ldo, _stream(codes)),
+           "dequantize rows=%d k=%d ldo=%d" % (rows, k, ldo))
+    return out
+
+
+def fake_quantize(x, global_scale=None, out_dtype=None):
+    """Quantise then dequantise ([P1] 접근 방법: exactly the 4-bit rounding
+    error, nothing else).  Two launches: nvfp4_quantize and
+    nvfp4_dequantize.  out_dtype defaults to x's dtype."""
+    q = quantize(x, global_scale)
+    return dequantize(q, out_dtype or x.dtype)
+
+
+def error_stats(x, q):
+    """Per-row float64 statistics of x and of its NVFP4 form q:
+    [rows, 3] = (sum x^2, sum (x - x_hat)^2, max |x|), x_hat the exact
+    dequantised value.  Relative error = sqrt(sum col 1 / sum col 0);
+    max/RMS of a row = col 2 / sqrt(col 0 / k)."""
+    _device_tensor(x, "x")
+    codes, scales, g = _nvfp4_parts(q, "q")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit stride along k")
+    dt = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}.get(x.dtype)
+    if dt is None:
+        raise ValueError("x must be float32 or bfloat16")
+    rows, k = x.shape
+    if codes.shape != (rows, k // 2) or scales.shape != (rows, k // 16):
+        raise ValueError("q does not match x's shape")
+    ldx = x.stride(0) if rows > 1 else k
+    stats = torch.empty((rows, 3), dtype=torch.float64, device=x.device)
+    _check(library().nvfp4_error_stats(_ptr(x), dt, rows, k, ldx, _ptr(codes),
+                                       _ptr(scales), _ptr(g), _ptr(stats),
+                                       _stream(x)),
+           "error_stats rows=%d k=%d ldx=%d" % (rows, k, ldx))
+    return stats

@@ -142,4 +142,51 @@ int w4a4_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                                       static_cast<hipStream_t>(stream)));
 }
 
+int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
+                     const float* global, int64_t rows, int64_t k, void* out,
+                     int out_dtype, int64_t ldo, void* stream) {
+  if (!codes || !scales || !global || !out) return NVFP4_ERR_INVALID_VALUE;
+  if (rows < 1 || k < 16 || k % 16 != 0 || ldo < k) return NVFP4_ERR_INVALID_VALUE;
+  if (rows > kMaxDim || ldo > kMaxDim || rows > kMaxDim / ldo)
+    return NVFP4_ERR_INVALID_VALUE;
+  if (rows * (k / 16) > (int64_t(1) << 39)) return NVFP4_ERR_INVALID_VALUE;
+  if (out_dtype != NVFP4_DTYPE_F32 && out_dtype != NVFP4_DTYPE_BF16)
+    return NVFP4_ERR_UNSUPPORTED;
+  const int64_t os = out_dtype == NVFP4_DTYPE_F32 ? 4 : 2;
+  if (!aligned(codes, 8) || !aligned(out, 16) || (ldo * os) % 16 != 0 ||
+      !aligned(global, 4))
+    return NVFP4_ERR_MISALIGNED;
+  const int64_t obytes = ((rows - 1) * ldo + k) * os;
+  if (overlap(out, obytes, codes, rows * (k / 2)) ||
+      overlap(out, obytes, scales, rows * (k / 16)) || overlap(out, obytes, global, 4))
+    return NVFP4_ERR_INVALID_VALUE;
+  return status_of(nvfp4::launch_dequantize(codes, scales, global, rows, k, out,
+                                            out_dtype, ldo,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int nvfp4_error_stats(const void* x, int x_dtype, int64_t rows, int64_t k,
+                      int64_t ldx, const uint8_t* codes, const uint8_t* scales,
+                      const float* global, double* stats, void* stream) {
+  if (!x || !codes || !scales || !global || !stats) return NVFP4_ERR_INVALID_VALUE;
+  if (rows < 1 || k < 16 || k % 16 != 0 || ldx < k) return NVFP4_ERR_INVALID_VALUE;
+  if (rows > kMaxDim || ldx > kMaxDim || rows > kMaxDim / ldx)
+    return NVFP4_ERR_INVALID_VALUE;
+  if (rows * (k / 16) > (int64_t(1) << 39)) return NVFP4_ERR_INVALID_VALUE;
+  if (x_dtype != NVFP4_DTYPE_F32 && x_dtype != NVFP4_DTYPE_BF16)
+    return NVFP4_ERR_UNSUPPORTED;
+  const int64_t es = x_dtype == NVFP4_DTYPE_F32 ? 4 : 2;
+  if (!aligned(x, 16) || (ldx * es) % 16 != 0 || !aligned(codes, 8) ||
+      !aligned(global, 4) || !aligned(stats, 8))
+    return NVFP4_ERR_MISALIGNED;
+  const int64_t sbytes = rows * 3 * 8;
+  if (overlap(stats, sbytes, x, ((rows - 1) * ldx + k) * es) ||
+      overlap(stats, sbytes, codes, rows * (k / 2)) ||
+      overlap(stats, sbytes, scales, rows * (k / 16)) || overlap(stats, sbytes, global, 4))
+    return NVFP4_ERR_INVALID_VALUE;
+  return status_of(nvfp4::launch_error_stats(x, x_dtype, rows, k, ldx, codes, scales,
+                                             global, stats,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -1,0 +1,217 @@
+// NVFP4 dequantisation and quantisation-error statistics for gfx950.
+//
+// Value of an element: sign * E2M1 * E4M3 * g (the format of the explainer
+// page "論文解説: Gated DeltaNet はなぜ4bit量子化に耐えるのか", section 前提1, and
+// of the arxiv-wiki page on the same paper, section 접근 방법).  e2m1 * e4m3
+// has at most 6 significant bits and is exact in binary32; times the
+// binary32 global the exact value has at most 30, so:
+//   * binary32 output: one IEEE multiply, a single rounding;
+//   * bfloat16 output: the exact product rounded to binary32 with
+//     round-to-odd and then to bfloat16 to nearest even, which equals one
+//     rounding of the exact value (binary32 keeps 16 more bits).
+// Error statistics (the A4 / W4 error percentages and max/RMS of the
+// input statistics on the arxiv-wiki page, section 접근 방법): per row,
+// in float64, sum x^2, sum (x - x_hat)^2 and max |x|.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "formats.h"
+#include "internal.h"
+
+namespace nvfp4 {
+namespace {
+
+constexpr int kDtypeF32 = 0;
+constexpr int kOutF32 = 0;
+
+// e2m1 * e4m3 of the 16 codes of a block (8 bytes), exact in binary32.
+__device__ __forceinline__ void decode_block(uint2 c, float sc, float* v) {
+  const unsigned w[2] = {c.x, c.y};
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      typedef float f32x2 __attribute__((ext_vector_type(2)));
+      const f32x2 p = j == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[h], 1.0f, 0)
+                    : j == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[h], 1.0f, 1)
+                    : j == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[h], 1.0f, 2)
+                             : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[h], 1.0f, 3);
+      v[8 * h + 2 * j] = p[0] * sc;
+      v[8 * h + 2 * j + 1] = p[1] * sc;
+    }
+}
+
+__device__ __forceinline__ unsigned short bf16_rne_bits(float f) {
+  const unsigned u = __float_as_uint(f);
+  return static_cast<unsigned short>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Nearest-even bfloat16 of the exact product v * g (v = e2m1 * e4m3, exact):
+// round to binary32 with round-to-odd, then to bfloat16.  For a product of
+// normal magnitude the binary32 residual fma(v, g, -f) is exact, so its sign
+// says whether f was rounded away from zero; near the subnormal range the
+// exact product is formed in float64 instead.
+__device__ __forceinline__ unsigned short bf16_of_product(float v, float g) {
+  float f = v * g;
+  if (__builtin_fabsf(f) >= 0x1p-100f) {
+    const float e = __builtin_fmaf(v, g, -f);   // exact - f, exactly
+    if (e != 0.0f) {
+      unsigned b = __float_as_uint(f);
+      if ((e < 0.0f) != (f < 0.0f)) b -= 1u;     // f was rounded away from zero
+      f = __uint_as_float(b | 1u);
+    }
+    return bf16_rne_bits(f);
+  }
+  const double p = static_cast<double>(v) * static_cast<double>(g);   // exact
+  f = static_cast<float>(p);
+  if (static_cast<double>(f) != p) {
+    unsigned b = __float_as_uint(f);
+    if (__builtin_fabs(static_cast<double>(f)) > __builtin_fabs(p)) b -= 1u;   // toward zero
+    f = __uint_as_float(b | 1u);
+  }
+  return bf16_rne_bits(f);
+}
+
+// One 16-element block per lane: 8 code bytes + 1 scale byte in, 16 values
+// out (64 or 32 contiguous bytes per lane, so a wave's stores coalesce;
+// non-temporal, as the output is a stream).
+template <int OUT>
+__global__ void __launch_bounds__(256)
+dequantize_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                  const float* __restrict__ global, int64_t nblocks, int64_t kb,
+                  void* __restrict__ out, int64_t ldo) {
+  const float g = *global;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t b = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+       b < nblocks; b += stride) {
+    const uint2 c = reinterpret_cast<const uint2*>(codes)[b];
+    const float sc = e4m3_f32(scales[b]);
+    float v[16];
+    decode_block(c, sc, v);
+    const int64_t row = b / kb, col = (b - row * kb) * 16;
+    if constexpr (OUT == kOutF32) {
+      typedef float f32x4 __attribute__((ext_vector_type(4)));
+      f32x4* o = reinterpret_cast<f32x4*>(static_cast<float*>(out) + row * ldo + col);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 t = {v[4 * q] * g, v[4 * q + 1] * g, v[4 * q + 2] * g, v[4 * q + 3] * g};
+        __builtin_nontemporal_store(t, o + q);
+      }
+    } else {
+      unsigned w[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const unsigned lo = bf16_of_product(v[2 * q], g);
+        const unsigned hi = bf16_of_product(v[2 * q + 1], g);
+        w[q] = lo | (hi << 16);
+      }
+      typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+      u32x4* o = reinterpret_cast<u32x4*>(static_cast<unsigned short*>(out) + row * ldo + col);
+      const u32x4 t0 = {w[0], w[1], w[2], w[3]}, t1 = {w[4], w[5], w[6], w[7]};
+      __builtin_nontemporal_store(t0, o);
+      __builtin_nontemporal_store(t1, o + 1);
+    }
+  }
+}
+
+// 16 input values of a block as binary32 (exact from bf16 or fp32).
+template <int DTYPE>
+__device__ __forceinline__ void load_values(const uint8_t* src, float* x) {
+  if constexpr (DTYPE == kDtypeF32) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 t = reinterpret_cast<const float4*>(src)[q];
+      x[4 * q] = t.x; x[4 * q + 1] = t.y; x[4 * q + 2] = t.z; x[4 * q + 3] = t.w;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint4 t = reinterpret_cast<const uint4*>(src)[q];
+      const unsigned w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[8 * q + 2 * i] = __uint_as_float(w[i] << 16);
+        x[8 * q + 2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+    }
+  }
+}
+
+// One wave per row: lane l takes blocks l, l + 64, ...; float64 sums are
+// reduced across the wave.  stats[row] = {sum x^2, sum (x - x_hat)^2, max|x|}.
+template <int DTYPE>
+__global__ void __launch_bounds__(256)
+error_stats_kernel(const uint8_t* __restrict__ x, int64_t rows, int64_t kb,
+                   int64_t ldx_bytes, const uint8_t* __restrict__ codes,
+                   const uint8_t* __restrict__ scales, const float* __restrict__ global,
+                   double* __restrict__ stats) {
+  constexpr int kElemBytes = DTYPE == kDtypeF32 ? 4 : 2;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= rows) return;   // whole waves leave together
+  const double g = static_cast<double>(*global);
+  double sx = 0.0, se = 0.0;
+  unsigned mx = 0u;
+  for (int64_t b = lane; b < kb; b += 64) {
+    float xv[16], v[16];
+    load_values<DTYPE>(x + row * ldx_bytes + b * (16 * kElemBytes), xv);
+    const int64_t blk = row * kb + b;
+    decode_block(reinterpret_cast<const uint2*>(codes)[blk], e4m3_f32(scales[blk]), v);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const double xd = static_cast<double>(xv[i]);
+      const double d = xd - static_cast<double>(v[i]) * g;
+      sx = __builtin_fma(xd, xd, sx);
+      se = __builtin_fma(d, d, se);
+      mx = max(mx, __float_as_uint(xv[i]) & 0x7FFFFFFFu);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    sx += __shfl_xor(sx, off);
+    se += __shfl_xor(se, off);
+    mx = max(mx, static_cast<unsigned>(__shfl_xor(static_cast<int>(mx), off)));
+  }
+  if (lane == 0) {
+    stats[3 * row] = sx;
+    stats[3 * row + 1] = se;
+    stats[3 * row + 2] = static_cast<double>(__uint_as_float(mx));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales,
+                             const float* global, int64_t rows, int64_t k,
+                             void* out, int out_dtype, int64_t ldo,
+                             hipStream_t stream) {
+  const int64_t kb = k / 16, nblocks = rows * kb;
+  const int64_t want = (nblocks + 255) / 256;
+  const unsigned grid = static_cast<unsigned>(want < 0x7FFFFFFF ? want : 0x7FFFFFFF);
+  if (out_dtype == kOutF32)
+    dequantize_kernel<0><<<grid, 256, 0, stream>>>(codes, scales, global, nblocks, kb, out, ldo);
+  else
+    dequantize_kernel<1><<<grid, 256, 0, stream>>>(codes, scales, global, nblocks, kb, out, ldo);
+  return hipGetLastError();
+}
+
+hipError_t launch_error_stats(const void* x, int x_dtype, int64_t rows, int64_t k,
+                              int64_t ldx, const uint8_t* codes,
+                              const uint8_t* scales, const float* global,
+                              double* stats, hipStream_t stream) {
+  const int64_t esize = x_dtype == kDtypeF32 ? 4 : 2;
+  const int64_t want = (rows + 3) / 4;
+  if (want > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const unsigned grid = static_cast<unsigned>(want);
+  const uint8_t* xb = static_cast<const uint8_t*>(x);
+  if (x_dtype == kDtypeF32)
+    error_stats_kernel<0><<<grid, 256, 0, stream>>>(xb, rows, k / 16, ldx * esize, codes,
+                                                    scales, global, stats);
+  else
+    error_stats_kernel<1><<<grid, 256, 0, stream>>>(xb, rows, k / 16, ldx * esize, codes,
+                                                    scales, global, stats);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

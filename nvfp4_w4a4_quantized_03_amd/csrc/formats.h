@@ -20,6 +20,12 @@ static __device__ __forceinline__ double e4m3_value(unsigned c) {
            : __builtin_ldexp(static_cast<double>(m), -9);
 }
 
+// binary32 value of a non-negative E4M3 code 0x00..0x7E (exact).
+static __device__ __forceinline__ float e4m3_f32(unsigned c) {
+  return c >= 8u ? __uint_as_float((c << 20) + 0x3C000000u)
+                 : static_cast<float>(c) * 0x1p-9f;
+}
+
 // A code within one step of RNE_SAT_E4M3(q) for q >= 0: q is rounded to
 // binary32 (clamped) and then rounded to 3 mantissa bits in integer form.
 static __device__ __forceinline__ unsigned e4m3_candidate(double q) {

@@ -29,4 +29,14 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                        void* out, int out_dtype, int64_t ldo, int epilogue,
                        hipStream_t stream);
 
+// Dequantisation and error statistics (dequantize.hip).
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales,
+                             const float* global, int64_t rows, int64_t k,
+                             void* out, int out_dtype, int64_t ldo,
+                             hipStream_t stream);
+hipError_t launch_error_stats(const void* x, int x_dtype, int64_t rows, int64_t k,
+                              int64_t ldx, const uint8_t* codes,
+                              const uint8_t* scales, const float* global,
+                              double* stats, hipStream_t stream);
+
 }  // namespace nvfp4

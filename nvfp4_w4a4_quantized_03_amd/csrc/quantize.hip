@@ -129,12 +129,6 @@ __device__ __forceinline__ unsigned e4m3_bracket(float q, bool* exact) {
   return pk & 0xFFu;
 }
 
-// binary32 value of an E4M3 code 0x00..0x7E (exact).
-__device__ __forceinline__ float e4m3_f32(unsigned c) {
-  return c >= 8u ? __uint_as_float((c << 20) + 0x3C000000u)
-                 : static_cast<float>(c) * 0x1p-9f;
-}
-
 // Exact code magnitude of an element whose two bracketed candidates are the
 // adjacent codes lo and lo + 1: compare |x| with the midpoint between them
 // times e4m3(s) g.  mid * e4m3(s) has <= 7 significant bits (exact in

@@ -33,7 +33,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert set(names) >= {"nvfp4_quantize", "nvfp4_harmonize_group",
-                          "w4a4_gemm", "nvfp4_status_string",
+                          "w4a4_gemm", "nvfp4_dequantize",
+                          "nvfp4_error_stats", "nvfp4_status_string",
                           "nvfp4_abi_version"}
     for name in names:
         assert hasattr(lib, name), name
@@ -114,6 +115,42 @@ def test_gemm_validation(lib):
     assert gm(lib, out=P + 0x600002) == MISALIGNED
     assert gm(lib, out=P + 0x300010) == INVALID       # out overlaps b codes
     assert gm(lib, out=P + 0x200000 - 8) == INVALID   # out covers a_global
+
+
+def dq(lib, codes=P, scales=P + 0x100000, g=P + 0x200000, rows=4, k=32,
+       out=P + 0x300000, od=1, ldo=32):
+    return lib.nvfp4_dequantize(codes, scales, g, rows, k, out, od, ldo, None)
+
+
+def test_dequantize_validation(lib):
+    for kw in ("codes", "scales", "g", "out"):
+        assert dq(lib, **{kw: None}) == INVALID, kw
+    assert dq(lib, rows=0) == INVALID
+    assert dq(lib, k=24, ldo=24) == INVALID
+    assert dq(lib, ldo=16) == INVALID                 # ldo < k
+    assert dq(lib, od=4) == UNSUPPORTED
+    assert dq(lib, codes=P + 4) == MISALIGNED
+    assert dq(lib, out=P + 0x300008) == MISALIGNED
+    assert dq(lib, ldo=36) == MISALIGNED              # bf16 row stride 72 B
+    assert dq(lib, out=P + 0x100000) == INVALID       # out covers the scales
+
+
+def es(lib, x=P, dt=1, rows=4, k=32, ldx=32, codes=P + 0x100000,
+       scales=P + 0x200000, g=P + 0x300000, stats=P + 0x400000):
+    return lib.nvfp4_error_stats(x, dt, rows, k, ldx, codes, scales, g,
+                                 stats, None)
+
+
+def test_error_stats_validation(lib):
+    for kw in ("x", "codes", "scales", "g", "stats"):
+        assert es(lib, **{kw: None}) == INVALID, kw
+    assert es(lib, rows=0) == INVALID
+    assert es(lib, k=40, ldx=40) == INVALID
+    assert es(lib, ldx=16) == INVALID
+    assert es(lib, dt=2) == UNSUPPORTED
+    assert es(lib, x=P + 8) == MISALIGNED
+    assert es(lib, stats=P + 0x400004) == MISALIGNED
+    assert es(lib, stats=P + 0x100000) == INVALID     # stats covers codes
 
 
 def test_binding_rejects_cpu_tensors():
