@@ -33,7 +33,7 @@ from .quantize import (quantize, quantize_exact, dequantize, global_scale,
                        dequantize_bf16, error_stats)
 from .harmonize import harmonize, harmonize_exact
 from .gemm import (gemm_exact_int, gemm_f64, gemm_f64_rows_cols, gate_alpha,
-                   gate_beta, decoded_units)
+                   gate_beta, decoded_units, gdn_gates)
 
 __all__ = [
     "E2M1_MAG", "e2m1_decode", "e4m3_decode", "e4m3_decode_table",
@@ -44,5 +44,5 @@ __all__ = [
     "dequantize_f32", "dequantize_bf16", "error_stats",
     "harmonize", "harmonize_exact",
     "gemm_exact_int", "gemm_f64", "gemm_f64_rows_cols", "gate_alpha",
-    "gate_beta", "decoded_units",
+    "gate_beta", "decoded_units", "gdn_gates",
 ]

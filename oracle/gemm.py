@@ -87,3 +87,19 @@ def gate_beta(y):
     """Write-strength gate beta = sigmoid(y), float64."""
     y = np.asarray(y, dtype=np.float64)
     return 1.0 / (1.0 + np.exp(-y))
+
+
+def gdn_gates(y, n_beta, a_log, dt_bias):
+    """The gate pair of one Gated DeltaNet layer from the fused b|a
+    projection output y [m, n_beta + n_alpha] (float64): beta = sigmoid of
+    the first n_beta columns, alpha = exp(-exp(A_log) * softplus(a + dt_bias))
+    of the rest, per column ([P3] 前提2: a through softplus and an
+    exponential in log space, b through a sigmoid; A_log and dt_bias are
+    the per-head log-space parameters).  Returns (beta, alpha)."""
+    y = np.asarray(y, dtype=np.float64)
+    a_log = np.asarray(a_log, dtype=np.float64)
+    dt_bias = np.asarray(dt_bias, dtype=np.float64)
+    beta = gate_beta(y[:, :n_beta])
+    sp = np.logaddexp(0.0, y[:, n_beta:] + dt_bias[None, :])
+    alpha = np.exp(-np.exp(a_log)[None, :] * sp)
+    return beta, alpha

@@ -592,3 +592,33 @@ def test_error_stats_against_fractions_and_invariants():
     c1, s1, g1 = oracle.quantize(one)
     st1 = oracle.error_stats(one, c1, s1, g1)
     assert st1[0, 2] / np.sqrt(st1[0, 0] / 16) == 4.0
+
+
+def test_gdn_gates_closed_forms_and_scalar_math():
+    """The full gate pair: with A_log = dt_bias = 0 alpha is the
+    exp(-softplus) gate; point values against Python's math module term by
+    term; limits and monotonicity in A_log and dt_bias."""
+    import math
+    rng = np.random.default_rng(2)
+    y = rng.standard_normal((5, 7)) * 4
+    b0, a0 = oracle.gdn_gates(y, 3, np.zeros(4), np.zeros(4))
+    assert np.array_equal(a0, oracle.gate_alpha(y[:, 3:]))
+    assert np.allclose(b0, scipy.special.expit(y[:, :3]), rtol=1e-15, atol=0)
+    a_log = np.array([-1.5, 0.0, 0.7, 2.0])
+    dt = np.array([0.3, -2.0, 1.1, 0.0])
+    _, a = oracle.gdn_gates(y, 3, a_log, dt)
+    for i in range(5):
+        for j in range(4):
+            x = y[i, 3 + j] + dt[j]
+            sp = x + math.log1p(math.exp(-x)) if x > 0 else math.log1p(math.exp(x))
+            want = math.exp(-math.exp(a_log[j]) * sp)
+            assert abs(a[i, j] - want) <= 1e-14 * want
+    _, half = oracle.gdn_gates(np.zeros((1, 2)), 1, np.zeros(1), np.zeros(1))
+    assert half[0, 0] == 0.5
+    _, near1 = oracle.gdn_gates(np.zeros((1, 2)), 1, np.array([-60.0]), np.zeros(1))
+    assert 1 - 1e-12 < near1[0, 0] <= 1.0
+    _, lo = oracle.gdn_gates(y, 3, a_log, dt)
+    _, hi = oracle.gdn_gates(y, 3, a_log + 0.5, dt)
+    assert np.all(hi <= lo)          # larger A_log forgets faster
+    _, more = oracle.gdn_gates(y, 3, a_log, dt + 0.5)
+    assert np.all(more <= lo)        # larger bias forgets faster
