@@ -131,7 +131,8 @@ def _time(fn, reps, stream):
 def other_workloads(nv, synth, dev, stream, reps=10):
     """Kernel timings of the other workloads at hidden size 5120 (inputs
     resident in HBM): in_proj 4096x12288, gate projections 32768x64 with
-    alpha/beta epilogues, a harmonised fused group (N = 17536), the tiny
+    alpha/beta epilogues and as one fused b|a GEMM with the full gate pair,
+    a harmonised fused group (N = 17536), the tiny
     16x128x256 case, the self-calibrated (COMPUTE) activation quantize, and
     dequantisation to bf16 plus per-row error statistics of the 32768x5120
     activations."""
@@ -171,6 +172,23 @@ def other_workloads(nv, synth, dev, stream, reps=10):
         res[name + "_" + epi] = {"gemm_us": t, "gbps": byts / t / 1e3,
                                  "frac_hbm_peak": byts / t / 1e3 / PEAK_HBM_GBPS}
     out["gate_proj_32768x64x5120"] = res
+    # the same two projections as one fused b|a GEMM with the full gate pair
+    codes = torch.empty((128, 2560), dtype=torch.uint8, device=dev)
+    scales = torch.empty((128, 320), dtype=torch.uint8, device=dev)
+    gmod = torch.empty(2, dtype=torch.float32, device=dev)
+    for i, name in enumerate(("w_b", "w_a")):
+        q = nv.quantize(up(3, name), out=(codes[64 * i:64 * (i + 1)], scales[64 * i:64 * (i + 1)]))
+        gmod[i:i + 1].copy_(q.global_scale)
+    wba = nv.NVFP4(codes, scales, nv.harmonize_group(scales, 5120, [0, 64, 128], gmod))
+    a_log = torch.linspace(-2.0, 1.5, 64, device=dev)
+    dt_bias = torch.linspace(-3.0, 3.0, 64, device=dev)
+    gb = (torch.empty((32768, 64), dtype=torch.float32, device=dev),
+          torch.empty((32768, 64), dtype=torch.float32, device=dev))
+    t = _time(lambda: nv.gdn_gates(qx, wba, 64, a_log, dt_bias, out=gb), reps, stream)
+    byts = 32768 * 5120 * 0.5625 + 128 * 5120 * 0.5625 + 32768 * 128 * 4
+    out["gdn_gates_fused_ba_32768x128x5120"] = {
+        "gemm_us": t, "gbps": byts / t / 1e3,
+        "frac_hbm_peak": byts / t / 1e3 / PEAK_HBM_GBPS}
     del x, qx
     # harmonised fused group 12288|5120|128 with X[8192x5120]
     sizes = [12288, 5120, 128]

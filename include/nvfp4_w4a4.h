@@ -161,6 +161,39 @@ int w4a4_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
               void* stream);
 
 /*
+ * w4a4_gemm_gdn_gates -- the gate pair of one Gated DeltaNet layer from
+ * its fused b|a gate projection ([P1] 개발자 관점 names the b/a fused
+ * group; [P3] 前提2: b through a sigmoid, a through softplus and an
+ * exponential in log space):
+ *   y      = (g_x g_w) * X_hat W_hat^T, W = [W_b ; W_a] (n_beta + n_alpha
+ *            rows, one harmonised global; see nvfp4_harmonize_group),
+ *   beta   = sigmoid(y[:, j]),                      j <  n_beta,
+ *   alpha  = exp(-exp(A_log[i]) * softplus(y[:, n_beta + i] + dt_bias[i])).
+ *
+ *   x_codes, x_scales, x_global  activations X [m][k] (NVFP4, as above).
+ *   w_codes, w_scales, w_global  fused weight [n_beta + n_alpha][k].
+ *   n_beta, n_alpha  >= 0, 1 <= n_beta + n_alpha <= 256 (else
+ *                UNSUPPORTED); k % 128 == 0 (else UNSUPPORTED); codes and
+ *                scale arrays 16-byte aligned (else MISALIGNED).
+ *   a_log, dt_bias  device, [n_alpha] floats (may be NULL if n_alpha == 0).
+ *   beta_out     device, out, [m][ld_beta] floats, ld_beta >= n_beta (NULL
+ *                allowed if n_beta == 0).
+ *   alpha_out    device, out, [m][ld_alpha] floats, ld_alpha >= n_alpha
+ *                (NULL allowed if n_alpha == 0).  Outputs must not overlap
+ *                each other or the inputs.
+ *
+ * y is computed as in w4a4_gemm (exact decode, fp32 accumulation, global
+ * factors on the fp32 sum); the gates in fp32.
+ */
+int w4a4_gemm_gdn_gates(const uint8_t* x_codes, const uint8_t* x_scales,
+                        const float* x_global, int64_t m,
+                        const uint8_t* w_codes, const uint8_t* w_scales,
+                        const float* w_global, int64_t n_beta, int64_t n_alpha,
+                        int64_t k, const float* a_log, const float* dt_bias,
+                        float* beta_out, int64_t ld_beta, float* alpha_out,
+                        int64_t ld_alpha, void* stream);
+
+/*
  * nvfp4_dequantize -- values of an NVFP4 tensor, the inverse map used for
  * fake quantisation (quantise, then dequantise) in the mechanism study of
  * [P1] 접근 방법; element value sign * E2M1 * E4M3 * g per [P3] 前提1.

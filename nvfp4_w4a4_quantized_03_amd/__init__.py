@@ -17,7 +17,8 @@ from collections import namedtuple
 
 import torch
 
-__all__ = ["NVFP4", "quantize", "harmonize_group", "gemm", "dequantize",
+__all__ = ["NVFP4", "quantize", "harmonize_group", "gemm", "gdn_gates",
+           "dequantize",
            "fake_quantize", "error_stats", "library",
            "LIB_PATH", "NVFP4Error"]
 
@@ -62,6 +63,9 @@ def library():
     L.w4a4_gemm.argtypes = [vp, vp, vp, i64, vp, vp, vp, i64, i64, vp, i32,
                             i64, i32, vp]
     L.w4a4_gemm.restype = i32
+    L.w4a4_gemm_gdn_gates.argtypes = [vp, vp, vp, i64, vp, vp, vp, i64, i64,
+                                      i64, vp, vp, vp, i64, vp, i64, vp]
+    L.w4a4_gemm_gdn_gates.restype = i32
     L.nvfp4_dequantize.argtypes = [vp, vp, vp, i64, i64, vp, i32, i64, vp]
     L.nvfp4_dequantize.restype = i32
     L.nvfp4_error_stats.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp,
@@ -270,3 +274,40 @@ def error_stats(x, q):
                                        _stream(x)),
            "error_stats rows=%d k=%d ldx=%d" % (rows, k, ldx))
     return stats
+
+
+def gdn_gates(x, w_ba, n_beta, a_log, dt_bias, out=None):
+    """Gate pair of a Gated DeltaNet layer from its fused b|a projection:
+    w_ba is the NVFP4 weight [W_b; W_a] (n_beta + n_alpha rows, one shared
+    global), x the NVFP4 activations [m, k].  Returns (beta [m, n_beta],
+    alpha [m, n_alpha]) float32 with beta = sigmoid(b) and
+    alpha = exp(-exp(A_log) * softplus(a + dt_bias)); a_log and dt_bias are
+    float32 GPU tensors [n_alpha].  out=(beta, alpha) supplies buffers."""
+    xc, xs, xg = _nvfp4_parts(x, "x")
+    wc, ws, wg = _nvfp4_parts(w_ba, "w_ba")
+    m, k = xc.shape[0], xc.shape[1] * 2
+    n = wc.shape[0]
+    n_alpha = n - n_beta
+    if wc.shape[1] * 2 != k or not 0 <= n_beta <= n:
+        raise ValueError("x and w_ba disagree in k, or n_beta is out of range")
+    for t, nm in ((a_log, "a_log"), (dt_bias, "dt_bias")):
+        _device_tensor(t, nm)
+        if t.dtype != torch.float32 or t.numel() != n_alpha or not t.is_contiguous():
+            raise ValueError("%s must be float32 [n_alpha]" % nm)
+    if out is None:
+        beta = torch.empty((m, n_beta), dtype=torch.float32, device=xc.device)
+        alpha = torch.empty((m, n_alpha), dtype=torch.float32, device=xc.device)
+    else:
+        beta, alpha = out
+    for t, nm, cols in ((beta, "beta", n_beta), (alpha, "alpha", n_alpha)):
+        if t.dtype != torch.float32 or t.shape != (m, cols) or t.stride(1) != 1:
+            raise ValueError("%s must be float32 [m, %d] with unit column stride" % (nm, cols))
+    ldb = beta.stride(0) if m > 1 else max(n_beta, 1)
+    lda = alpha.stride(0) if m > 1 else max(n_alpha, 1)
+    _check(library().w4a4_gemm_gdn_gates(
+        _ptr(xc), _ptr(xs), _ptr(xg), m, _ptr(wc), _ptr(ws), _ptr(wg), n_beta,
+        n_alpha, k, _ptr(a_log), _ptr(dt_bias),
+        _ptr(beta) if n_beta else None, ldb,
+        _ptr(alpha) if n_alpha else None, lda, _stream(xc)),
+        "gdn_gates m=%d n_beta=%d n_alpha=%d k=%d" % (m, n_beta, n_alpha, k))
+    return beta, alpha

@@ -142,6 +142,53 @@ int w4a4_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                                       static_cast<hipStream_t>(stream)));
 }
 
+int w4a4_gemm_gdn_gates(const uint8_t* x_codes, const uint8_t* x_scales,
+                        const float* x_global, int64_t m,
+                        const uint8_t* w_codes, const uint8_t* w_scales,
+                        const float* w_global, int64_t n_beta, int64_t n_alpha,
+                        int64_t k, const float* a_log, const float* dt_bias,
+                        float* beta_out, int64_t ld_beta, float* alpha_out,
+                        int64_t ld_alpha, void* stream) {
+  if (!x_codes || !x_scales || !x_global || !w_codes || !w_scales || !w_global)
+    return NVFP4_ERR_INVALID_VALUE;
+  if (m < 1 || n_beta < 0 || n_alpha < 0 || n_beta + n_alpha < 1 || k < 16 ||
+      k % 16 != 0 || m > kMaxDim || k > kMaxDim || m > kMaxDim / k)
+    return NVFP4_ERR_INVALID_VALUE;
+  if (n_beta > 0 && (!beta_out || ld_beta < n_beta || m > kMaxDim / ld_beta))
+    return NVFP4_ERR_INVALID_VALUE;
+  if (n_alpha > 0 && (!alpha_out || !a_log || !dt_bias || ld_alpha < n_alpha ||
+                      m > kMaxDim / ld_alpha))
+    return NVFP4_ERR_INVALID_VALUE;
+  if (n_beta + n_alpha > nvfp4::kMaxGateCols || k % 128 != 0)
+    return NVFP4_ERR_UNSUPPORTED;
+  if (!aligned(x_codes, 16) || !aligned(w_codes, 16) || !aligned(x_scales, 16) ||
+      !aligned(w_scales, 16) || !aligned(x_global, 4) || !aligned(w_global, 4) ||
+      (n_beta > 0 && !aligned(beta_out, 4)) ||
+      (n_alpha > 0 && (!aligned(alpha_out, 4) || !aligned(a_log, 4) ||
+                       !aligned(dt_bias, 4))))
+    return NVFP4_ERR_MISALIGNED;
+  const int64_t n = n_beta + n_alpha;
+  struct Range { const void* p; int64_t len; };
+  const Range in[] = {{x_codes, m * (k / 2)}, {x_scales, m * (k / 16)},
+                      {x_global, 4}, {w_codes, n * (k / 2)},
+                      {w_scales, n * (k / 16)}, {w_global, 4},
+                      {a_log, 4 * n_alpha}, {dt_bias, 4 * n_alpha}};
+  const Range outs[] = {{beta_out, n_beta ? ((m - 1) * ld_beta + n_beta) * 4 : 0},
+                        {alpha_out, n_alpha ? ((m - 1) * ld_alpha + n_alpha) * 4 : 0}};
+  for (const Range& o : outs) {
+    if (o.len == 0) continue;
+    for (const Range& i : in)
+      if (i.len > 0 && overlap(o.p, o.len, i.p, i.len)) return NVFP4_ERR_INVALID_VALUE;
+  }
+  if (outs[0].len && outs[1].len && overlap(outs[0].p, outs[0].len, outs[1].p, outs[1].len))
+    return NVFP4_ERR_INVALID_VALUE;
+  return status_of(nvfp4::launch_gdn_gates(x_codes, x_scales, x_global, m, w_codes,
+                                           w_scales, w_global, n_beta, n_alpha, k,
+                                           a_log, dt_bias, beta_out, ld_beta,
+                                           alpha_out, ld_alpha,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
                      const float* global, int64_t rows, int64_t k, void* out,
                      int out_dtype, int64_t ldo, void* stream) {

@@ -39,6 +39,18 @@ constexpr int kOutF32 = 0;
 constexpr int kEpiNone = 0;
 constexpr int kEpiAlpha = 1;
 constexpr int kEpiBeta = 2;
+constexpr int kEpiGdn = 3;   // gate pair of a fused b|a projection (skinny kernel only)
+
+// Arguments of the gate-pair epilogue: columns [0, n_beta) of the product
+// give beta (stored to `out`), the others alpha with per-column A_log and
+// dt_bias (stored to out2 at column col - n_beta).
+struct EpiArgs {
+  const float* a_log;
+  const float* dt_bias;
+  int64_t n_beta;
+  float* out2;
+  int64_t ldo2;
+};
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -66,6 +78,14 @@ __device__ __forceinline__ half8_t decode8(unsigned codes, half2_t sc) {
 __device__ __forceinline__ unsigned short f32_to_bf16_rne(float f) {
   const unsigned u = __float_as_uint(f);
   return static_cast<unsigned short>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// e^x from the hardware base-2 exponential (v_exp_f32, about 1 ulp):
+// 2^(x log2 e); the rounding of x log2 e adds |x| 2^-24 relative error.
+constexpr float kLog2e = 1.44269504088896341f;
+constexpr float kLn2 = 0.693147180559945309f;
+__device__ __forceinline__ float exp_hw(float x) {
+  return __builtin_amdgcn_exp2f(x * kLog2e);
 }
 
 template <int EPI>
@@ -826,7 +846,7 @@ w4a4_gemm_skinny(const uint8_t* __restrict__ a_codes,
                  const uint8_t* __restrict__ b_codes,
                  const uint8_t* __restrict__ b_scales,
                  const float* __restrict__ b_global, int64_t n, int64_t k,
-                 void* __restrict__ out, int64_t ldo, int tiles_n) {
+                 void* __restrict__ out, int64_t ldo, int tiles_n, EpiArgs ep) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 31, h = lane >> 5;
   const int64_t m0 = static_cast<int64_t>(blockIdx.x / tiles_n) * (32 * TMT);
@@ -910,7 +930,8 @@ w4a4_gemm_skinny(const uint8_t* __restrict__ a_codes,
 #pragma unroll
     for (int e = 0; e < 16; ++e) red[wave][e][lane] = acc[ti][tj][e];
     __syncthreads();
-#pragma unroll
+    // not unrolled: the gate epilogue's code stays out of the tile loop
+#pragma unroll 1
     for (int v0 = 0; v0 < 16 * 64; v0 += NWV * 64) {
       const int v = v0 + threadIdx.x;
       if (NWV * 64 <= 16 * 64 || v < 16 * 64) {
@@ -921,11 +942,25 @@ w4a4_gemm_skinny(const uint8_t* __restrict__ a_codes,
         const int64_t row = m0 + ti * 32 + 8 * (e >> 2) + (l >> 5) * 4 + (e & 3);
         const int64_t col = n0 + tj * 32 + (l & 31);
         if (row < m && col < n) {
-          const float y = epilogue<EPI>(static_cast<float>(static_cast<double>(sum) * gab));
-          if constexpr (OUT == kOutF32)
-            static_cast<float*>(out)[row * ldo + col] = y;
-          else
-            static_cast<unsigned short*>(out)[row * ldo + col] = f32_to_bf16_rne(y);
+          const float y = static_cast<float>(static_cast<double>(sum) * gab);
+          if constexpr (EPI == kEpiGdn) {
+            if (col < ep.n_beta) {
+              static_cast<float*>(out)[row * ldo + col] =
+                  __builtin_amdgcn_rcpf(1.0f + exp_hw(-y));
+            } else {
+              // alpha = exp(-exp(A_log) softplus(a + dt_bias)),
+              // softplus(x) = max(x, 0) + log(1 + e^-|x|)
+              const int64_t j = col - ep.n_beta;
+              const float x = y + ep.dt_bias[j];
+              const float sp = fmaxf(x, 0.0f) +
+                               __builtin_amdgcn_logf(1.0f + exp_hw(-fabsf(x))) * kLn2;
+              ep.out2[row * ep.ldo2 + j] = exp_hw(-exp_hw(ep.a_log[j]) * sp);
+            }
+          } else if constexpr (OUT == kOutF32) {
+            static_cast<float*>(out)[row * ldo + col] = epilogue<EPI>(y);
+          } else {
+            static_cast<unsigned short*>(out)[row * ldo + col] = f32_to_bf16_rne(epilogue<EPI>(y));
+          }
         }
       }
     }
@@ -937,18 +972,19 @@ hipError_t launch_skinny(const uint8_t* a_codes, const uint8_t* a_scales,
                          const float* a_global, int64_t m,
                          const uint8_t* b_codes, const uint8_t* b_scales,
                          const float* b_global, int64_t n, int64_t k,
-                         void* out, int64_t ldo, hipStream_t stream) {
+                         void* out, int64_t ldo, hipStream_t stream,
+                         EpiArgs ep = EpiArgs{}) {
   const int64_t tm = (m + 32 * TMT - 1) / (32 * TMT), tn = (n + 32 * TNT - 1) / (32 * TNT);
   if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
   const unsigned grid = static_cast<unsigned>(tm * tn);
   if (k % 256 == 0)
     w4a4_gemm_skinny<TMT, TNT, NWV, KG, 4, OUT, EPI><<<grid, NWV * 64, 0, stream>>>(
         a_codes, a_scales, a_global, m, b_codes, b_scales, b_global, n, k, out, ldo,
-        static_cast<int>(tn));
+        static_cast<int>(tn), ep);
   else
     w4a4_gemm_skinny<TMT, TNT, NWV, 2 * KG, 2, OUT, EPI><<<grid, NWV * 64, 0, stream>>>(
         a_codes, a_scales, a_global, m, b_codes, b_scales, b_global, n, k, out, ldo,
-        static_cast<int>(tn));
+        static_cast<int>(tn), ep);
   return hipGetLastError();
 }
 
@@ -1030,6 +1066,23 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
   if (epilogue == kEpiBeta) return dispatch_align<1, kEpiBeta>(NVFP4_GEMM_ARGS);
   return dispatch_align<1, kEpiNone>(NVFP4_GEMM_ARGS);
 #undef NVFP4_GEMM_ARGS
+}
+
+hipError_t launch_gdn_gates(const uint8_t* x_codes, const uint8_t* x_scales,
+                            const float* x_global, int64_t m,
+                            const uint8_t* w_codes, const uint8_t* w_scales,
+                            const float* w_global, int64_t n_beta, int64_t n_alpha,
+                            int64_t k, const float* a_log, const float* dt_bias,
+                            float* beta_out, int64_t ld_beta, float* alpha_out,
+                            int64_t ld_alpha, hipStream_t stream) {
+  const int64_t n = n_beta + n_alpha;
+  const EpiArgs ep{a_log, dt_bias, n_beta, alpha_out, ld_alpha};
+#define NVFP4_GDN_ARGS x_codes, x_scales, x_global, m, w_codes, w_scales, w_global, n, k, \
+                       beta_out, ld_beta, stream, ep
+  if (n <= 64) return launch_skinny<2, 2, 4, 1, kOutF32, kEpiGdn>(NVFP4_GDN_ARGS);
+  if (n <= 128) return launch_skinny<2, 4, 8, 1, kOutF32, kEpiGdn>(NVFP4_GDN_ARGS);
+  return launch_skinny<1, 8, 4, 1, kOutF32, kEpiGdn>(NVFP4_GDN_ARGS);
+#undef NVFP4_GDN_ARGS
 }
 
 }  // namespace nvfp4

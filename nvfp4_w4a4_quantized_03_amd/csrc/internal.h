@@ -29,6 +29,17 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                        void* out, int out_dtype, int64_t ldo, int epilogue,
                        hipStream_t stream);
 
+// Gate pair of a fused b|a projection (gemm.hip); k % 128 == 0, 16-byte
+// aligned scale arrays and n_beta + n_alpha <= 256 are checked by the caller.
+constexpr int64_t kMaxGateCols = 256;
+hipError_t launch_gdn_gates(const uint8_t* x_codes, const uint8_t* x_scales,
+                            const float* x_global, int64_t m,
+                            const uint8_t* w_codes, const uint8_t* w_scales,
+                            const float* w_global, int64_t n_beta, int64_t n_alpha,
+                            int64_t k, const float* a_log, const float* dt_bias,
+                            float* beta_out, int64_t ld_beta, float* alpha_out,
+                            int64_t ld_alpha, hipStream_t stream);
+
 // Dequantisation and error statistics (dequantize.hip).
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales,
                              const float* global, int64_t rows, int64_t k,

@@ -33,7 +33,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert set(names) >= {"nvfp4_quantize", "nvfp4_harmonize_group",
-                          "w4a4_gemm", "nvfp4_dequantize",
+                          "w4a4_gemm", "w4a4_gemm_gdn_gates",
+                          "nvfp4_dequantize",
                           "nvfp4_error_stats", "nvfp4_status_string",
                           "nvfp4_abi_version"}
     for name in names:
@@ -115,6 +116,30 @@ def test_gemm_validation(lib):
     assert gm(lib, out=P + 0x600002) == MISALIGNED
     assert gm(lib, out=P + 0x300010) == INVALID       # out overlaps b codes
     assert gm(lib, out=P + 0x200000 - 8) == INVALID   # out covers a_global
+
+
+def gg(lib, xc=P, xs=P + 0x100000, xg=P + 0x200000, m=4, wc=P + 0x300000,
+       ws=P + 0x400000, wg=P + 0x500000, nb=8, na=8, k=128, al=P + 0x600000,
+       dt=P + 0x700000, bo=P + 0x800000, ldb=8, ao=P + 0x900000, lda=8):
+    return lib.w4a4_gemm_gdn_gates(xc, xs, xg, m, wc, ws, wg, nb, na, k, al, dt,
+                                   bo, ldb, ao, lda, None)
+
+
+def test_gdn_gates_validation(lib):
+    for kw in ("xc", "xs", "xg", "wc", "ws", "wg", "al", "dt", "bo", "ao"):
+        assert gg(lib, **{kw: None}) == INVALID, kw
+    assert gg(lib, nb=0, na=0) == INVALID
+    assert gg(lib, m=0) == INVALID
+    assert gg(lib, nb=-1) == INVALID
+    assert gg(lib, k=24) == INVALID
+    assert gg(lib, ldb=4) == INVALID                  # ld_beta < n_beta
+    assert gg(lib, lda=4) == INVALID
+    assert gg(lib, k=192) == UNSUPPORTED              # k % 128 != 0
+    assert gg(lib, nb=200, na=100, ldb=200, lda=100) == UNSUPPORTED
+    assert gg(lib, xs=P + 0x100008) == MISALIGNED     # scales not 16-byte aligned
+    assert gg(lib, ao=P + 0x900002) == MISALIGNED
+    assert gg(lib, ao=P + 0x800010) == INVALID        # alpha overlaps beta
+    assert gg(lib, bo=P + 0x300000) == INVALID        # beta over the weight codes
 
 
 def dq(lib, codes=P, scales=P + 0x100000, g=P + 0x200000, rows=4, k=32,

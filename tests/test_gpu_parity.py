@@ -495,3 +495,64 @@ def test_calls_on_a_side_stream():
     check_quant(xv, q)
     ref = oracle.gemm_exact_int(*oracle.quantize(xv), *oracle.quantize(xv))
     assert rel_frob(host(y).astype(np.float64), ref) <= TOL
+
+
+# ----------------------------------------- gate pair of a fused b|a projection
+
+def _gate_params(n_alpha, seed):
+    rng = np.random.default_rng(seed)
+    a_log = rng.uniform(-2.0, 1.5, n_alpha).astype(np.float32)
+    dt = rng.uniform(-3.0, 3.0, n_alpha).astype(np.float32)
+    return a_log, dt, torch.from_numpy(a_log).to(DEV), torch.from_numpy(dt).to(DEV)
+
+
+@pytest.mark.parametrize("m,n_beta,n_alpha,k", [(1, 16, 16, 128), (37, 64, 64, 5120),
+                                                (300, 32, 48, 384), (513, 100, 120, 256),
+                                                (64, 0, 20, 128), (40, 24, 0, 256),
+                                                (70, 128, 128, 640)])
+def test_gdn_gates(m, n_beta, n_alpha, k):
+    rng = np.random.default_rng(m + n_beta + 3 * n_alpha + k)
+    xv = rng.standard_normal((m, k)).astype(np.float32)
+    wv = (rng.standard_normal((n_beta + n_alpha, k)) * 0.05).astype(np.float32)
+    _say("gdn gates", m, n_beta, n_alpha, k)
+    a_log, dt, a_dev, dt_dev = _gate_params(n_alpha, k)
+    qa = nv.quantize(up(xv, None, "f32"))
+    qb = nv.quantize(up(wv, None, "f32"))
+    y = oracle.gemm_exact_int(*oracle.quantize(xv), *oracle.quantize(wv))
+    beta_ref, alpha_ref = oracle.gdn_gates(y, n_beta, a_log, dt)
+    beta, alpha = nv.gdn_gates(qa, qb, n_beta, a_dev, dt_dev)
+    if n_beta:
+        assert rel_frob(host(beta).astype(np.float64), beta_ref) <= TOL
+    if n_alpha:
+        assert rel_frob(host(alpha).astype(np.float64), alpha_ref) <= TOL
+
+
+def test_gdn_gates_harmonized_group_full_size():
+    """32768 tokens x hidden 5120 through the b|a group (64 + 64 heads), the
+    two weights quantised with their own globals and harmonised into one
+    fused buffer; sampled rows against the oracle."""
+    k, nb, na = 5120, 64, 64
+    xv, xb, xt = workload(3, "x")
+    wav, wab, wat = workload(3, "w_a")
+    wbv, wbb, wbt = workload(3, "w_b")
+    _say("gdn gates full size 32768x128x5120")
+    codes = torch.empty((nb + na, k // 2), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((nb + na, k // 16), dtype=torch.uint8, device=DEV)
+    gdev = torch.empty(2, dtype=torch.float32, device=DEV)
+    for i, (v, b, t, lo, hi) in enumerate(((wbv, wbb, wbt, 0, nb), (wav, wab, wat, nb, nb + na))):
+        q = nv.quantize(up(v, b, t), out=(codes[lo:hi], scales[lo:hi]))
+        gdev[i:i + 1].copy_(q.global_scale)
+    gstar = nv.harmonize_group(scales, k, [0, nb, nb + na], gdev)
+    qa = nv.quantize(up(xv, xb, xt))
+    a_log, dt, a_dev, dt_dev = _gate_params(na, 77)
+    beta, alpha = nv.gdn_gates(qa, nv.NVFP4(codes, scales, gstar), nb, a_dev, dt_dev)
+    rows = sample_rows(32768, 128, 43)
+    ca, sa, ga = oracle.quantize(xv[rows], g=oracle.global_scale(xv))
+    gs = [oracle.global_scale(wbv), oracle.global_scale(wav)]
+    pb, pa = oracle.quantize(wbv, g=gs[0]), oracle.quantize(wav, g=gs[1])
+    bs_h, g_ref = oracle.harmonize(np.concatenate([pb[1], pa[1]]), [0, nb, nb + na], gs)
+    y = oracle.gemm_f64(ca, sa, ga, np.concatenate([pb[0], pa[0]]), bs_h, g_ref)
+    beta_ref, alpha_ref = oracle.gdn_gates(y, nb, a_log, dt)
+    sel = torch.from_numpy(rows).to(DEV)
+    assert rel_frob(host(beta[sel]).astype(np.float64), beta_ref) <= TOL
+    assert rel_frob(host(alpha[sel]).astype(np.float64), alpha_ref) <= TOL
