@@ -32,6 +32,8 @@ from .quantize import (quantize, quantize_exact, dequantize, global_scale,
                        unpack_codes, pack_codes, dequantize_f32,
                        dequantize_bf16, error_stats)
 from .harmonize import harmonize, harmonize_exact
+from .fp8kv import (kv_amax, kv_scale, kv_cast, kv_decode, kv_cast_exact,
+                    kv_scale_exact)
 from .gemm import (gemm_exact_int, gemm_f64, gemm_f64_rows_cols, gate_alpha,
                    gate_beta, decoded_units, gdn_gates)
 
@@ -43,6 +45,8 @@ __all__ = [
     "unpack_codes", "pack_codes", "block_scales", "encode_elements",
     "dequantize_f32", "dequantize_bf16", "error_stats",
     "harmonize", "harmonize_exact",
+    "kv_amax", "kv_scale", "kv_cast", "kv_decode", "kv_cast_exact",
+    "kv_scale_exact",
     "gemm_exact_int", "gemm_f64", "gemm_f64_rows_cols", "gate_alpha",
     "gate_beta", "decoded_units", "gdn_gates",
 ]

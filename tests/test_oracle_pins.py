@@ -622,3 +622,51 @@ def test_gdn_gates_closed_forms_and_scalar_math():
     assert np.all(hi <= lo)          # larger A_log forgets faster
     _, more = oracle.gdn_gates(y, 3, a_log, dt + 0.5)
     assert np.all(more <= lo)        # larger bias forgets faster
+
+
+# --------------------------------------------------- FP8 KV static scales
+
+def test_kv_cast_matches_torch_float8_in_range():
+    """With s = 2^e the codes are torch's float8_e4m3fn cast of x / 2^e
+    (exact scaling), for every in-range bf16 value and both signs."""
+    mags = _bf16_nonneg_finite()
+    for e in (0, -5, 7):
+        s = np.float32(2.0 ** e)
+        v = mags[mags <= 448 * float(s)]
+        x = np.concatenate([v, -v]).astype(np.float32)
+        ref = torch.from_numpy(x / np.float32(s)).to(torch.float8_e4m3fn) \
+            .view(torch.uint8).numpy()
+        got = oracle.kv_cast(x, s)
+        # torch keeps -0 as 0x80 like the oracle; compare everything
+        assert np.array_equal(got, ref), e
+
+
+def test_kv_cast_fast_equals_exact_with_midpoints_and_saturation():
+    rng = np.random.default_rng(8)
+    s = np.float32(0.0137)
+    mids = [(oracle.e4m3_decode(c) + oracle.e4m3_decode(c + 1)) / 2
+            for c in range(0, 126, 7)]
+    x = [float(np.float32(float(m) * float(s))) for m in mids]
+    x += list((rng.standard_normal(200) * 3).astype(np.float32))
+    x += [1e6, -1e6, 0.0, -0.0, 448 * float(s), 1e-30]
+    x = np.array(x, dtype=np.float32)[None, :]
+    assert np.array_equal(oracle.kv_cast(x, s),
+                          np.array(oracle.kv_cast_exact(x.tolist(), s), dtype=np.uint8))
+    c = oracle.kv_cast(x, s)[0]
+    assert c[-6] == 0x7E and c[-5] == 0xFE and c[-4] == 0x00 and c[-3] == 0x80
+    assert np.all(oracle.kv_cast(x, 0.0) & 0x7F == 0)
+
+
+def test_kv_scale_is_one_correct_rounding_and_maps_amax_to_448():
+    rng = np.random.default_rng(4)
+    a = np.concatenate([rng.random(2000) * 1e3, rng.random(200) * 1e-40,
+                        [448.0, 1.0, 3.0 * 2 ** -140]]).astype(np.float32)
+    for v in a:
+        assert float(oracle.kv_scale(v)) == oracle.kv_scale_exact(v)
+    x = (rng.standard_normal((16, 64)) * 5).astype(np.float32)
+    s = oracle.kv_scale(oracle.kv_amax([x[:8], x[8:]]))
+    assert oracle.kv_amax([x[:8], x[8:]]) == np.max(np.abs(x))
+    c = oracle.kv_cast(x, s)
+    assert np.max(c & 0x7F) == 0x7E               # the largest magnitude saturates at 448
+    rel = np.linalg.norm(oracle.kv_decode(c, s) - x) / np.linalg.norm(x)
+    assert rel < 2 ** -4                           # 3 mantissa bits
