@@ -135,7 +135,8 @@ def other_workloads(nv, synth, dev, stream, reps=10):
     a harmonised fused group (N = 17536), the tiny
     16x128x256 case, the self-calibrated (COMPUTE) activation quantize, and
     dequantisation to bf16 plus per-row error statistics of the 32768x5120
-    activations."""
+    activations, and the FP8 KV-cache scale calibration and cast of a
+    32768x1024 bf16 slab."""
     import numpy as np
     import torch
 
@@ -240,6 +241,18 @@ def other_workloads(nv, synth, dev, stream, reps=10):
         "error_stats_us": t_e,
         "error_stats_gbps_2.5625B_per_elem": elems * 2.5625 / t_e / 1e3,
         "error_stats_frac_hbm_peak": elems * 2.5625 / t_e / 1e3 / PEAK_HBM_GBPS}
+    del yb, q, xv
+    # FP8 KV cache: calibrate a static scale, cast a 32768 x 1024 bf16 slab
+    kvx = torch.randn((32768, 1024), device=dev).to(torch.bfloat16)
+    scale, amax = nv.fp8_kv_calibrate([kvx])
+    kvo = torch.empty((32768, 1024), dtype=torch.uint8, device=dev)
+    t_a = _time(lambda: nv.fp8_kv_calibrate([kvx], amax=amax), reps, stream)
+    t_k = _time(lambda: nv.fp8_kv_cast(kvx, scale, out=kvo), reps, stream)
+    kv_el = 32768 * 1024
+    out["fp8_kv_32768x1024_bf16"] = {
+        "calibrate_us": t_a, "calibrate_gbps_2B_per_elem": kv_el * 2 / t_a / 1e3,
+        "cast_us": t_k, "cast_gbps_3B_per_elem": kv_el * 3 / t_k / 1e3,
+        "cast_frac_hbm_peak": kv_el * 3 / t_k / 1e3 / PEAK_HBM_GBPS}
     return out
 
 

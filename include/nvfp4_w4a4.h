@@ -234,6 +234,30 @@ int nvfp4_error_stats(const void* x, int x_dtype, int64_t rows, int64_t k,
                       int64_t ldx, const uint8_t* codes, const uint8_t* scales,
                       const float* global, double* stats, void* stream);
 
+/*
+ * FP8 KV cache with a static per-tensor scale ([P1] 접근 방법 and the
+ * abstract on the paper's listing page: store the KV cache in FP8 and ship
+ * calibrated per-tensor scales with the checkpoint).  OCP E4M3 codes; the
+ * scale is a decode factor s = fp32(amax / 448) over the calibration data;
+ * a stored code is sign(x) | E4M3(|x| / s), the exact quotient rounded once
+ * to nearest, ties to the even code, saturating at 448 (magnitude 0 when
+ * s == 0).  Decoded value: e4m3(code) * s.
+ *
+ * fp8_kv_amax_update -- *amax = max(*amax, max |x|) over a calibration
+ *   tensor x [rows][ldx] (same rules as nvfp4_quantize's x).  *amax is a
+ *   device float the caller sets to 0 before the first call; calls on one
+ *   amax accumulate.
+ * fp8_kv_scale_from_amax -- *scale = fp32(*amax / 448) (device floats).
+ * fp8_kv_cast -- out [rows][ldo] bytes (16-byte aligned, ldo >= k,
+ *   ldo % 16 == 0) = codes of x [rows][ldx] under the device scale *scale
+ *   (finite, >= 0).  out must not overlap x or the scale.
+ */
+int fp8_kv_amax_update(const void* x, int x_dtype, int64_t rows, int64_t k,
+                       int64_t ldx, float* amax, void* stream);
+int fp8_kv_scale_from_amax(const float* amax, float* scale, void* stream);
+int fp8_kv_cast(const void* x, int x_dtype, int64_t rows, int64_t k, int64_t ldx,
+                const float* scale, uint8_t* out, int64_t ldo, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* nvfp4_status_string(int status);
 

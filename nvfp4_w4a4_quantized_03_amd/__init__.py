@@ -18,7 +18,7 @@ from collections import namedtuple
 import torch
 
 __all__ = ["NVFP4", "quantize", "harmonize_group", "gemm", "gdn_gates",
-           "dequantize",
+           "dequantize", "fp8_kv_calibrate", "fp8_kv_cast",
            "fake_quantize", "error_stats", "library",
            "LIB_PATH", "NVFP4Error"]
 
@@ -66,6 +66,12 @@ def library():
     L.w4a4_gemm_gdn_gates.argtypes = [vp, vp, vp, i64, vp, vp, vp, i64, i64,
                                       i64, vp, vp, vp, i64, vp, i64, vp]
     L.w4a4_gemm_gdn_gates.restype = i32
+    L.fp8_kv_amax_update.argtypes = [vp, i32, i64, i64, i64, vp, vp]
+    L.fp8_kv_amax_update.restype = i32
+    L.fp8_kv_scale_from_amax.argtypes = [vp, vp, vp]
+    L.fp8_kv_scale_from_amax.restype = i32
+    L.fp8_kv_cast.argtypes = [vp, i32, i64, i64, i64, vp, vp, i64, vp]
+    L.fp8_kv_cast.restype = i32
     L.nvfp4_dequantize.argtypes = [vp, vp, vp, i64, i64, vp, i32, i64, vp]
     L.nvfp4_dequantize.restype = i32
     L.nvfp4_error_stats.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp,
@@ -311,3 +317,48 @@ def gdn_gates(x, w_ba, n_beta, a_log, dt_bias, out=None):
         _ptr(alpha) if n_alpha else None, lda, _stream(xc)),
         "gdn_gates m=%d n_beta=%d n_alpha=%d k=%d" % (m, n_beta, n_alpha, k))
     return beta, alpha
+
+
+def _x_args(x, name="x"):
+    _device_tensor(x, name)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("%s must be 2-D with unit stride along k" % name)
+    dt = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}.get(x.dtype)
+    if dt is None:
+        raise ValueError("%s must be float32 or bfloat16" % name)
+    rows, k = x.shape
+    return dt, rows, k, (x.stride(0) if rows > 1 else k)
+
+
+def fp8_kv_calibrate(tensors, amax=None):
+    """Static per-tensor FP8 KV scale from calibration tensors (float32 or
+    bfloat16 GPU tensors [rows, k]): the running max |x| is accumulated on
+    the device (pass amax, a float32 [1] GPU tensor, to continue an earlier
+    calibration), then scale = fp32(amax / 448).  Returns (scale, amax)."""
+    first = tensors[0]
+    if amax is None:
+        amax = torch.zeros(1, dtype=torch.float32, device=first.device)
+    for t in tensors:
+        dt, rows, k, ldx = _x_args(t, "calibration tensor")
+        _check(library().fp8_kv_amax_update(_ptr(t), dt, rows, k, ldx, _ptr(amax),
+                                            _stream(t)), "fp8_kv_amax_update")
+    scale = torch.empty(1, dtype=torch.float32, device=first.device)
+    _check(library().fp8_kv_scale_from_amax(_ptr(amax), _ptr(scale), _stream(first)),
+           "fp8_kv_scale_from_amax")
+    return scale, amax
+
+
+def fp8_kv_cast(x, scale, out=None):
+    """OCP E4M3 codes (uint8 [rows, k]) of x under the static decode scale
+    (float32 [1] GPU tensor): sign | E4M3(|x| / scale), one rounding."""
+    dt, rows, k, ldx = _x_args(x)
+    _device_tensor(scale, "scale")
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.uint8, device=x.device)
+    elif out.dtype != torch.uint8 or out.shape != (rows, k) or out.stride(1) != 1:
+        raise ValueError("out must be uint8 [rows, k] with unit column stride")
+    ldo = out.stride(0) if rows > 1 else k
+    _check(library().fp8_kv_cast(_ptr(x), dt, rows, k, ldx, _ptr(scale), _ptr(out),
+                                 ldo, _stream(x)),
+           "fp8_kv_cast rows=%d k=%d ldx=%d ldo=%d" % (rows, k, ldx, ldo))
+    return out

@@ -236,4 +236,51 @@ int nvfp4_error_stats(const void* x, int x_dtype, int64_t rows, int64_t k,
                                              static_cast<hipStream_t>(stream)));
 }
 
+// Shared checks of a [rows][k] input tensor x (k % 16 == 0, ldx >= k,
+// 16-byte aligned rows).  Returns NVFP4_OK or the status to report.
+static int check_x(const void* x, int x_dtype, int64_t rows, int64_t k, int64_t ldx) {
+  if (!x) return NVFP4_ERR_INVALID_VALUE;
+  if (rows < 1 || k < 16 || k % 16 != 0 || ldx < k) return NVFP4_ERR_INVALID_VALUE;
+  if (rows > kMaxDim || ldx > kMaxDim || rows > kMaxDim / ldx)
+    return NVFP4_ERR_INVALID_VALUE;
+  if (rows * (k / 16) > (int64_t(1) << 39)) return NVFP4_ERR_INVALID_VALUE;
+  if (x_dtype != NVFP4_DTYPE_F32 && x_dtype != NVFP4_DTYPE_BF16)
+    return NVFP4_ERR_UNSUPPORTED;
+  const int64_t es = x_dtype == NVFP4_DTYPE_F32 ? 4 : 2;
+  if (!aligned(x, 16) || (ldx * es) % 16 != 0) return NVFP4_ERR_MISALIGNED;
+  return NVFP4_OK;
+}
+
+int fp8_kv_amax_update(const void* x, int x_dtype, int64_t rows, int64_t k,
+                       int64_t ldx, float* amax, void* stream) {
+  const int st = check_x(x, x_dtype, rows, k, ldx);
+  if (st != NVFP4_OK) return st;
+  if (!amax) return NVFP4_ERR_INVALID_VALUE;
+  if (!aligned(amax, 4)) return NVFP4_ERR_MISALIGNED;
+  return status_of(nvfp4::launch_kv_amax_update(x, x_dtype, rows, k, ldx, amax,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int fp8_kv_scale_from_amax(const float* amax, float* scale, void* stream) {
+  if (!amax || !scale) return NVFP4_ERR_INVALID_VALUE;
+  if (!aligned(amax, 4) || !aligned(scale, 4)) return NVFP4_ERR_MISALIGNED;
+  return status_of(nvfp4::launch_kv_scale(amax, scale, static_cast<hipStream_t>(stream)));
+}
+
+int fp8_kv_cast(const void* x, int x_dtype, int64_t rows, int64_t k, int64_t ldx,
+                const float* scale, uint8_t* out, int64_t ldo, void* stream) {
+  const int st = check_x(x, x_dtype, rows, k, ldx);
+  if (st != NVFP4_OK) return st;
+  if (!scale || !out || ldo < k || ldo > kMaxDim || rows > kMaxDim / ldo)
+    return NVFP4_ERR_INVALID_VALUE;
+  if (!aligned(scale, 4) || !aligned(out, 16) || ldo % 16 != 0)
+    return NVFP4_ERR_MISALIGNED;
+  const int64_t es = x_dtype == NVFP4_DTYPE_F32 ? 4 : 2;
+  const int64_t obytes = (rows - 1) * ldo + k;
+  if (overlap(out, obytes, x, ((rows - 1) * ldx + k) * es) || overlap(out, obytes, scale, 4))
+    return NVFP4_ERR_INVALID_VALUE;
+  return status_of(nvfp4::launch_kv_cast(x, x_dtype, rows, k, ldx, scale, out, ldo,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -50,4 +50,12 @@ hipError_t launch_error_stats(const void* x, int x_dtype, int64_t rows, int64_t 
                               const uint8_t* scales, const float* global,
                               double* stats, hipStream_t stream);
 
+// FP8 KV cache with a static per-tensor scale (fp8kv.hip).
+hipError_t launch_kv_amax_update(const void* x, int x_dtype, int64_t rows, int64_t k,
+                                 int64_t ldx, float* amax, hipStream_t stream);
+hipError_t launch_kv_scale(const float* amax, float* scale, hipStream_t stream);
+hipError_t launch_kv_cast(const void* x, int x_dtype, int64_t rows, int64_t k,
+                          int64_t ldx, const float* scale, uint8_t* out,
+                          int64_t ldo, hipStream_t stream);
+
 }  // namespace nvfp4

@@ -34,7 +34,8 @@ def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
     assert set(names) >= {"nvfp4_quantize", "nvfp4_harmonize_group",
                           "w4a4_gemm", "w4a4_gemm_gdn_gates",
-                          "nvfp4_dequantize",
+                          "nvfp4_dequantize", "fp8_kv_amax_update",
+                          "fp8_kv_scale_from_amax", "fp8_kv_cast",
                           "nvfp4_error_stats", "nvfp4_status_string",
                           "nvfp4_abi_version"}
     for name in names:
@@ -176,6 +177,28 @@ def test_error_stats_validation(lib):
     assert es(lib, x=P + 8) == MISALIGNED
     assert es(lib, stats=P + 0x400004) == MISALIGNED
     assert es(lib, stats=P + 0x100000) == INVALID     # stats covers codes
+
+
+def kv(lib, x=P, dt=1, rows=4, k=32, ldx=32, scale=P + 0x100000,
+       out=P + 0x200000, ldo=32):
+    return lib.fp8_kv_cast(x, dt, rows, k, ldx, scale, out, ldo, None)
+
+
+def test_fp8_kv_validation(lib):
+    for kw in ("x", "scale", "out"):
+        assert kv(lib, **{kw: None}) == INVALID, kw
+    assert kv(lib, rows=0) == INVALID
+    assert kv(lib, k=24, ldx=24, ldo=24) == INVALID
+    assert kv(lib, ldo=16) == INVALID                 # ldo < k
+    assert kv(lib, dt=5) == UNSUPPORTED
+    assert kv(lib, x=P + 8) == MISALIGNED
+    assert kv(lib, out=P + 0x200008) == MISALIGNED
+    assert kv(lib, ldo=40) == MISALIGNED              # ldo % 16 != 0
+    assert kv(lib, out=P + 16) == INVALID             # out overlaps x
+    assert lib.fp8_kv_amax_update(P, 1, 4, 32, 32, None, None) == INVALID
+    assert lib.fp8_kv_amax_update(P, 1, 4, 32, 32, P + 2, None) == MISALIGNED
+    assert lib.fp8_kv_scale_from_amax(None, P, None) == INVALID
+    assert lib.fp8_kv_scale_from_amax(P, P + 1, None) == MISALIGNED
 
 
 def test_binding_rejects_cpu_tensors():
