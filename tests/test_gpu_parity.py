@@ -556,3 +556,47 @@ def test_gdn_gates_harmonized_group_full_size():
     sel = torch.from_numpy(rows).to(DEV)
     assert rel_frob(host(beta[sel]).astype(np.float64), beta_ref) <= TOL
     assert rel_frob(host(alpha[sel]).astype(np.float64), alpha_ref) <= TOL
+
+
+# ------------------------------------------------------ degenerate and limits
+
+def test_gemm_zero_operand_and_zero_global():
+    """An all-zero activation tensor quantises to g = 0 and zero scales; the
+    product is exactly +0 everywhere (pipelined and skinny shapes)."""
+    rng = np.random.default_rng(6)
+    for m, n, k in ((300, 200, 256), (16, 500, 512)):
+        xz = np.zeros((m, k), dtype=np.float32)
+        wv = rng.standard_normal((n, k)).astype(np.float32)
+        qa, qb = nv.quantize(up(xz, None, "f32")), nv.quantize(up(wv, None, "f32"))
+        assert host(qa.global_scale)[0] == 0.0
+        y = host(nv.gemm(qa, qb, out_dtype=torch.float32))
+        assert np.all(y == 0.0)
+
+
+@pytest.mark.parametrize("k", [1 << 22, (1 << 22) + 256])
+def test_gemm_longest_k_sparse_blocks(k):
+    """k at and past the largest K of the pipelined kernel's 32-bit tile
+    offsets (2^22; beyond it the staged kernel runs).  Random codes, block
+    scales zero except in a few blocks spread over K (first, middle, last),
+    so the exact reference only needs those blocks."""
+    m = n = 65
+    rng = np.random.default_rng(k)
+    _say("gemm longest k", k)
+    ac = rng.integers(0, 256, (m, k // 2), dtype=np.uint8)
+    bc = rng.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    kb = k // 16
+    live = np.array(sorted({0, 1, 7, kb // 2, kb // 2 + 1, (1 << 18) - 1,
+                            min(1 << 18, kb - 1), kb - 2, kb - 1}))
+    as_ = np.zeros((m, kb), dtype=np.uint8)
+    bs = np.zeros((n, kb), dtype=np.uint8)
+    as_[:, live] = rng.integers(1, 0x7F, (m, live.size))
+    bs[:, live] = rng.integers(1, 0x7F, (n, live.size))
+    ga, gb = np.float32(0.01), np.float32(0.003)
+
+    def dev(c, s, g):
+        return nv.NVFP4(torch.from_numpy(c).to(DEV), torch.from_numpy(s).to(DEV),
+                        torch.tensor([g], dtype=torch.float32, device=DEV))
+    y = host(nv.gemm(dev(ac, as_, ga), dev(bc, bs, gb), out_dtype=torch.float32))
+    cols = (live[:, None] * 8 + np.arange(8)[None, :]).ravel()     # code bytes of live blocks
+    ref = oracle.gemm_f64(ac[:, cols], as_[:, live], ga, bc[:, cols], bs[:, live], gb)
+    assert rel_frob(y.astype(np.float64), ref) <= TOL
