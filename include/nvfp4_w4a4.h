@@ -51,7 +51,8 @@ extern "C" {
 typedef enum {
     NVFP4_OK = 0,
     NVFP4_ERR_INVALID_VALUE = 1, /* null pointer, bad size, k % 16 != 0, ... */
-    NVFP4_ERR_UNSUPPORTED = 2,   /* unknown dtype / mode / epilogue          */
+    NVFP4_ERR_UNSUPPORTED = 2,   /* unknown dtype / mode / epilogue, or a    */
+                                 /* shape outside the call's kernels       */
     NVFP4_ERR_MISALIGNED = 3,    /* a pointer or stride breaks the alignment  */
     NVFP4_ERR_LAUNCH = 4         /* the HIP runtime refused a launch          */
 } nvfp4_status;
@@ -261,7 +262,8 @@ int fp8_kv_cast(const void* x, int x_dtype, int64_t rows, int64_t k, int64_t ldx
 /* Static text for a status code (never NULL). */
 const char* nvfp4_status_string(int status);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2 (1 plus w4a4_gemm_gdn_gates, nvfp4_dequantize,
+   nvfp4_error_stats and the fp8_kv_* calls). */
 int nvfp4_abi_version(void);
 
 #ifdef __cplusplus

@@ -29,11 +29,26 @@ int status_of(hipError_t e) {
   return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
 }
 
+// Shared checks of a [rows][k] input tensor x (k % 16 == 0, ldx >= k,
+// 16-byte aligned rows).  Returns NVFP4_OK or the status to report.
+int check_x(const void* x, int x_dtype, int64_t rows, int64_t k, int64_t ldx) {
+  if (!x) return NVFP4_ERR_INVALID_VALUE;
+  if (rows < 1 || k < 16 || k % 16 != 0 || ldx < k) return NVFP4_ERR_INVALID_VALUE;
+  if (rows > kMaxDim || ldx > kMaxDim || rows > kMaxDim / ldx)
+    return NVFP4_ERR_INVALID_VALUE;
+  if (rows * (k / 16) > (int64_t(1) << 39)) return NVFP4_ERR_INVALID_VALUE;
+  if (x_dtype != NVFP4_DTYPE_F32 && x_dtype != NVFP4_DTYPE_BF16)
+    return NVFP4_ERR_UNSUPPORTED;
+  const int64_t es = x_dtype == NVFP4_DTYPE_F32 ? 4 : 2;
+  if (!aligned(x, 16) || (ldx * es) % 16 != 0) return NVFP4_ERR_MISALIGNED;
+  return NVFP4_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int nvfp4_abi_version(void) { return 1; }
+int nvfp4_abi_version(void) { return 2; }
 
 const char* nvfp4_status_string(int status) {
   switch (status) {
@@ -42,7 +57,9 @@ const char* nvfp4_status_string(int status) {
       return "NVFP4_ERR_INVALID_VALUE: null pointer, bad size, k not a "
              "multiple of 16, bad stride or overlapping buffers";
     case NVFP4_ERR_UNSUPPORTED:
-      return "NVFP4_ERR_UNSUPPORTED: unknown dtype, global mode or epilogue";
+      return "NVFP4_ERR_UNSUPPORTED: unknown dtype, global mode or epilogue, "
+             "or a shape outside the call's kernels (gate pair: more than 256 "
+             "columns or k not a multiple of 128)";
     case NVFP4_ERR_MISALIGNED:
       return "NVFP4_ERR_MISALIGNED: a pointer or row stride breaks the "
              "required alignment";
@@ -234,21 +251,6 @@ int nvfp4_error_stats(const void* x, int x_dtype, int64_t rows, int64_t k,
   return status_of(nvfp4::launch_error_stats(x, x_dtype, rows, k, ldx, codes, scales,
                                              global, stats,
                                              static_cast<hipStream_t>(stream)));
-}
-
-// Shared checks of a [rows][k] input tensor x (k % 16 == 0, ldx >= k,
-// 16-byte aligned rows).  Returns NVFP4_OK or the status to report.
-static int check_x(const void* x, int x_dtype, int64_t rows, int64_t k, int64_t ldx) {
-  if (!x) return NVFP4_ERR_INVALID_VALUE;
-  if (rows < 1 || k < 16 || k % 16 != 0 || ldx < k) return NVFP4_ERR_INVALID_VALUE;
-  if (rows > kMaxDim || ldx > kMaxDim || rows > kMaxDim / ldx)
-    return NVFP4_ERR_INVALID_VALUE;
-  if (rows * (k / 16) > (int64_t(1) << 39)) return NVFP4_ERR_INVALID_VALUE;
-  if (x_dtype != NVFP4_DTYPE_F32 && x_dtype != NVFP4_DTYPE_BF16)
-    return NVFP4_ERR_UNSUPPORTED;
-  const int64_t es = x_dtype == NVFP4_DTYPE_F32 ? 4 : 2;
-  if (!aligned(x, 16) || (ldx * es) % 16 != 0) return NVFP4_ERR_MISALIGNED;
-  return NVFP4_OK;
 }
 
 int fp8_kv_amax_update(const void* x, int x_dtype, int64_t rows, int64_t k,

@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
                           "nvfp4_abi_version"}
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.nvfp4_abi_version() == 1
+    assert lib.nvfp4_abi_version() == 2
     for s in range(6):
         assert lib.nvfp4_status_string(s)
 
