@@ -357,8 +357,10 @@ w4a4_gemm_kernel(const uint8_t* __restrict__ a_codes,
     }
 }
 
+// LDS ring depth of the pipelined kernel (3 or 4 slots of 36 KB); 3 measured
+// ~1.5% faster than 4 (fewer loads outstanding per wave).
 #ifndef PIPE_STAGES
-#define PIPE_STAGES 4
+#define PIPE_STAGES 3
 #endif
 // Optional scheduling hint placed after a half-stage's fragment reads (empty:
 // with LDS waits counted precisely, forcing the reads to the front of the
@@ -377,15 +379,16 @@ w4a4_gemm_kernel(const uint8_t* __restrict__ a_codes,
 //   (r / 4) % 4 so that 16 lanes reading 16 consecutive rows hit 16 distinct
 //   bank groups.  Scales stay raw E4M3 (8 bytes per row per stage) and are
 //   widened to fp16 when an operand is decoded.
-// * NS = 4 LDS slots form a ring: stages kt + 1 .. kt + 3 are in flight or
-//   resident while stage kt is consumed, so the next half-stage's fragments
-//   are read one half ahead and the next k-step's operands are decoded while
-//   the 16 MFMAs of the current k-step issue.  Each stage issues the same
-//   loads (past the last stage they repeat it into the slot just freed),
-//   A's with the first k-step's MFMAs and B's with the fourth's; one wait
-//   that leaves the two newest fills in flight and one barrier per stage
-//   keep the ring ordered: stage kt + 3 goes into the slot of stage kt - 1,
-//   which every wave finished before the barrier that closed stage kt - 1.
+// * NS (3 or 4) LDS slots form a ring: stages kt + 1 .. kt + NS - 1 are in
+//   flight or resident while stage kt is consumed, so the next half-stage's
+//   fragments are read one half ahead and the next k-step's operands are
+//   decoded while the 16 MFMAs of the current k-step issue.  Each stage
+//   issues the same loads (past the last stage they repeat it into the slot
+//   just freed), A's with the first k-step's MFMAs and B's with the
+//   fourth's; one wait that leaves the NS - 2 newest fills in flight and one
+//   barrier per stage keep the ring ordered: stage kt + NS - 1 goes into the
+//   slot of stage kt - 1, which every wave finished before the barrier that
+//   closed stage kt - 1.
 // * Rows past m or n load a clamped (valid) row; their outputs are never
 //   stored.  Offsets within a tile are 32-bit, so the launcher takes this
 //   kernel only for k <= 2^22.
