@@ -451,13 +451,18 @@ __device__ __forceinline__ void decode_step(Operands<TM, TN>& o, const HalfFrags
   for (int i = 0; i < TN; ++i) o.b[i] = fb.operand(i, j);
 }
 
+// One k-step: TM x TN MFMAs in a zig-zag order (odd rows of tiles walk the B
+// tiles backwards, so consecutive MFMAs at a row change share their B
+// operand; ~1% faster than a plain row-major order).
 template <int TM, int TN>
 __device__ __forceinline__ void mfma_step(float16_t (&acc)[TM][TN], const Operands<TM, TN>& o) {
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+    for (int jj = 0; jj < TN; ++jj) {
+      const int j = (i & 1) ? TN - 1 - jj : jj;
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(o.a[i], o.b[j], acc[i][j], 0, 0, 0);
+    }
 }
 
 // Scheduling hint for one k-step: alternate one MFMA with a few VALU ops
