@@ -33,7 +33,7 @@ PEAK_MFMA_TFLOPS = 2500.0        # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBPS = 8000.0           # MI355X HBM3E
 M, M_DEC, N, K = 32768, 32, 10240, 5120
 WORKLOAD = 5
-KERNEL_SOURCES = ["gemm.hip", "quantize.hip"]
+KERNEL_SOURCES = ["gemm.hip", "quantize.hip", "quant_device.h"]
 
 
 def parse():
@@ -135,8 +135,9 @@ def other_workloads(nv, synth, dev, stream, reps=10):
     a harmonised fused group (N = 17536), the tiny
     16x128x256 case, the self-calibrated (COMPUTE) activation quantize, and
     dequantisation to bf16 plus per-row error statistics of the 32768x5120
-    activations, and the FP8 KV-cache scale calibration and cast of a
-    32768x1024 bf16 slab."""
+    activations, the decode projection's activation quantisation + GEMM as
+    two calls and as one fused launch, and the FP8 KV-cache scale
+    calibration and cast of a 32768x1024 bf16 slab."""
     import numpy as np
     import torch
 
@@ -242,6 +243,42 @@ def other_workloads(nv, synth, dev, stream, reps=10):
         "error_stats_gbps_2.5625B_per_elem": elems * 2.5625 / t_e / 1e3,
         "error_stats_frac_hbm_peak": elems * 2.5625 / t_e / 1e3 / PEAK_HBM_GBPS}
     del yb, q, xv
+    # decode projection 32 x 10240 x 5120: activation quantisation + GEMM as
+    # two library calls and as the one-launch fused call, with COMPUTE
+    # (self-calibrated) and GIVEN globals.  Direct C-ABI calls with
+    # pre-marshalled arguments keep the Python wrappers' host time out of
+    # the GPU timing of these short kernels.
+    import ctypes
+    lib = nv.library()
+    xd, qw = up(5, "x_dec"), nv.quantize(up(5, "w"))
+    qd = nv.quantize(xd)
+    g_given = qd.global_scale.clone()
+    g_out = torch.empty(1, dtype=torch.float32, device=dev)
+    yd = torch.empty((32, 10240), dtype=torch.bfloat16, device=dev)
+    sv = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    dec = {}
+    for mode, g in (("compute", g_out), ("given", g_given)):
+        mcode = nv.GLOBAL_COMPUTE if mode == "compute" else nv.GLOBAL_GIVEN
+        qargs = (P(xd), nv.DTYPE_BF16, 32, 5120, 5120, P(qd.codes), P(qd.scales), P(g),
+                 mcode, sv)
+        gargs = (P(qd.codes), P(qd.scales), P(g), 32, P(qw.codes), P(qw.scales),
+                 P(qw.global_scale), 10240, 5120, P(yd), nv.DTYPE_BF16, 10240, 0, sv)
+        fargs = (P(xd), nv.DTYPE_BF16, 32, 5120, 5120, P(qd.codes), P(qd.scales), P(g),
+                 mcode, P(qw.codes), P(qw.scales), P(qw.global_scale), 10240, P(yd),
+                 nv.DTYPE_BF16, 10240, sv)
+        assert lib.nvfp4_quantize(*qargs) == 0 and lib.w4a4_gemm(*gargs) == 0
+        assert lib.w4a4_gemm_quantize_a(*fargs) == 0
+
+        def separate():
+            lib.nvfp4_quantize(*qargs)
+            lib.w4a4_gemm(*gargs)
+        t_sep = _time(separate, 4 * reps, stream)
+        t_fus = _time(lambda: lib.w4a4_gemm_quantize_a(*fargs), 4 * reps, stream)
+        dec[mode] = {"separate_quantize_gemm_us": t_sep, "fused_us": t_fus,
+                     "fused_speedup": t_sep / t_fus}
+    out["decode_quantize_gemm_32x10240x5120"] = dec
+    del xd, qw, qd, yd
     # FP8 KV cache: calibrate a static scale, cast a 32768 x 1024 bf16 slab
     kvx = torch.randn((32768, 1024), device=dev).to(torch.bfloat16)
     scale, amax = nv.fp8_kv_calibrate([kvx])

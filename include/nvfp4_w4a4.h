@@ -195,6 +195,42 @@ int w4a4_gemm_gdn_gates(const uint8_t* x_codes, const uint8_t* x_scales,
                         int64_t ld_alpha, void* stream);
 
 /*
+ * w4a4_gemm_quantize_a -- small-M activation quantisation and W4A4 GEMM in
+ * one launch: nvfp4_quantize of X, then w4a4_gemm of the result with the
+ * weights (no epilogue).  For decode batches, where [P1] 한계 (limitations)
+ * puts a 2-4 % loss on the activation quantisation.
+ *
+ *   x, x_dtype, m, k, ldx  activations X [m][ldx] as for nvfp4_quantize;
+ *                1 <= m <= 64 and k % 128 == 0 (else UNSUPPORTED).
+ *   x_codes, x_scales, x_global, mode  out (x_global read in GIVEN mode):
+ *                the NVFP4 form of X, bit-identical to nvfp4_quantize with
+ *                the same mode; codes and scales 16-byte aligned.
+ *   w_codes, w_scales, w_global  weights W [n][k] (NVFP4; codes and scales
+ *                16-byte aligned), n >= 1.
+ *   out, out_dtype, ldo  Y [m][ldo] of F32 or BF16, ldo >= n, 4-byte
+ *                aligned.  Equal bit for bit to w4a4_gemm(x_codes, ..., W,
+ *                W4A4_EPI_NONE) on the same device.
+ * Outputs must not overlap each other or the inputs.
+ *
+ * One cooperative launch: the workgroups that own blocks of X quantise them
+ * (with COMPUTE, each of them first takes max |x| over all of X), a
+ * grid-wide barrier follows, then every workgroup computes GEMM tiles.  The
+ * grid is capped at the co-resident workgroup count of the device; larger
+ * shapes loop inside the kernel.  NVFP4_ERR_LAUNCH if the runtime refuses
+ * the cooperative launch.  Calls on different streams that share these
+ * buffers must be ordered by the caller.
+ * Cost: on MI355X a cooperative launch and its grid barrier cost more than
+ * the launches they save, so at decode sizes this call is slower than
+ * nvfp4_quantize followed by w4a4_gemm; it serves callers that need the
+ * whole step in one launch.
+ */
+int w4a4_gemm_quantize_a(const void* x, int x_dtype, int64_t m, int64_t k, int64_t ldx,
+                         uint8_t* x_codes, uint8_t* x_scales, float* x_global, int mode,
+                         const uint8_t* w_codes, const uint8_t* w_scales,
+                         const float* w_global, int64_t n, void* out, int out_dtype,
+                         int64_t ldo, void* stream);
+
+/*
  * nvfp4_dequantize -- values of an NVFP4 tensor, the inverse map used for
  * fake quantisation (quantise, then dequantise) in the mechanism study of
  * [P1] 접근 방법; element value sign * E2M1 * E4M3 * g per [P3] 前提1.
@@ -262,8 +298,9 @@ int fp8_kv_cast(const void* x, int x_dtype, int64_t rows, int64_t k, int64_t ldx
 /* Static text for a status code (never NULL). */
 const char* nvfp4_status_string(int status);
 
-/* ABI version of this header: 2 (1 plus w4a4_gemm_gdn_gates, nvfp4_dequantize,
-   nvfp4_error_stats and the fp8_kv_* calls). */
+/* ABI version of this header: 3 (1 plus w4a4_gemm_gdn_gates, nvfp4_dequantize,
+   nvfp4_error_stats and the fp8_kv_* calls in 2, plus w4a4_gemm_quantize_a
+   in 3). */
 int nvfp4_abi_version(void);
 
 #ifdef __cplusplus

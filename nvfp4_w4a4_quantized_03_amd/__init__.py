@@ -17,7 +17,8 @@ from collections import namedtuple
 
 import torch
 
-__all__ = ["NVFP4", "quantize", "harmonize_group", "gemm", "gdn_gates",
+__all__ = ["NVFP4", "quantize", "harmonize_group", "gemm", "gemm_quantize_a",
+           "gdn_gates",
            "dequantize", "fp8_kv_calibrate", "fp8_kv_cast",
            "fake_quantize", "error_stats", "library",
            "LIB_PATH", "NVFP4Error"]
@@ -72,6 +73,9 @@ def library():
     L.fp8_kv_scale_from_amax.restype = i32
     L.fp8_kv_cast.argtypes = [vp, i32, i64, i64, i64, vp, vp, i64, vp]
     L.fp8_kv_cast.restype = i32
+    L.w4a4_gemm_quantize_a.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, i32,
+                                       vp, vp, vp, i64, vp, i32, i64, vp]
+    L.w4a4_gemm_quantize_a.restype = i32
     L.nvfp4_dequantize.argtypes = [vp, vp, vp, i64, i64, vp, i32, i64, vp]
     L.nvfp4_dequantize.restype = i32
     L.nvfp4_error_stats.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp,
@@ -218,6 +222,46 @@ def gemm(a, b, out_dtype=torch.bfloat16, epilogue="none", out=None):
                                EPILOGUES[epilogue],
                                _stream(ac)))
     return out
+
+
+def gemm_quantize_a(x, w, global_scale=None, out_dtype=torch.bfloat16,
+                    out=None):
+    """Small-M (rows <= 64) activation quantisation and W4A4 GEMM in one
+    launch: quantize(x, global_scale), then gemm(that, w).  x: float32 or
+    bfloat16 GPU tensor [m, k] (k % 128 == 0); w: NVFP4 weights [n, k].
+    global_scale as for quantize (None: self-calibrated).  Returns
+    (NVFP4 of x, Y [m, n] of out_dtype), both bit-identical to the two
+    separate calls."""
+    dt, m, k, ldx = _x_args(x)
+    wc, ws, wg = _nvfp4_parts(w, "w")
+    n = wc.shape[0]
+    if wc.shape[1] * 2 != k or ws.shape != (n, k // 16):
+        raise ValueError("operand shapes disagree")
+    od = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}.get(out_dtype)
+    if od is None:
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    codes = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((m, k // 16), dtype=torch.uint8, device=x.device)
+    if global_scale is None:
+        g = torch.empty(1, dtype=torch.float32, device=x.device)
+        mode = GLOBAL_COMPUTE
+    else:
+        _device_tensor(global_scale, "global_scale")
+        if global_scale.dtype != torch.float32 or global_scale.numel() != 1:
+            raise ValueError("global_scale must be one float32")
+        g = global_scale
+        mode = GLOBAL_GIVEN
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    elif out.dtype != out_dtype or out.dim() != 2 or out.shape != (m, n) \
+            or out.stride(1) != 1:
+        raise ValueError("out has the wrong dtype, shape or layout")
+    _check(library().w4a4_gemm_quantize_a(
+        _ptr(x), dt, m, k, ldx, _ptr(codes), _ptr(scales), _ptr(g), mode,
+        _ptr(wc), _ptr(ws), _ptr(wg), n, _ptr(out), od,
+        out.stride(0) if m > 1 else n, _stream(x)),
+        "gemm_quantize_a m=%d n=%d k=%d" % (m, n, k))
+    return NVFP4(codes, scales, g), out
 
 
 def _nvfp4_parts(q, name):

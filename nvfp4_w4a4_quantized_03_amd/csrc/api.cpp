@@ -48,7 +48,7 @@ int check_x(const void* x, int x_dtype, int64_t rows, int64_t k, int64_t ldx) {
 
 extern "C" {
 
-int nvfp4_abi_version(void) { return 2; }
+int nvfp4_abi_version(void) { return 3; }
 
 const char* nvfp4_status_string(int status) {
   switch (status) {
@@ -59,7 +59,8 @@ const char* nvfp4_status_string(int status) {
     case NVFP4_ERR_UNSUPPORTED:
       return "NVFP4_ERR_UNSUPPORTED: unknown dtype, global mode or epilogue, "
              "or a shape outside the call's kernels (gate pair: more than 256 "
-             "columns or k not a multiple of 128)";
+             "columns or k not a multiple of 128; fused quantise + GEMM: more "
+             "than 64 rows or k not a multiple of 128)";
     case NVFP4_ERR_MISALIGNED:
       return "NVFP4_ERR_MISALIGNED: a pointer or row stride breaks the "
              "required alignment";
@@ -204,6 +205,47 @@ int w4a4_gemm_gdn_gates(const uint8_t* x_codes, const uint8_t* x_scales,
                                            a_log, dt_bias, beta_out, ld_beta,
                                            alpha_out, ld_alpha,
                                            static_cast<hipStream_t>(stream)));
+}
+
+int w4a4_gemm_quantize_a(const void* x, int x_dtype, int64_t m, int64_t k, int64_t ldx,
+                         uint8_t* x_codes, uint8_t* x_scales, float* x_global, int mode,
+                         const uint8_t* w_codes, const uint8_t* w_scales,
+                         const float* w_global, int64_t n, void* out, int out_dtype,
+                         int64_t ldo, void* stream) {
+  if (!x_codes || !x_scales || !x_global || !w_codes || !w_scales || !w_global || !out)
+    return NVFP4_ERR_INVALID_VALUE;
+  const int cx = check_x(x, x_dtype, m, k, ldx);
+  if (cx != NVFP4_OK) return cx;
+  if (n < 1 || ldo < n || n > kMaxDim || k > kMaxDim || ldo > kMaxDim ||
+      m > kMaxDim / ldo || n > kMaxDim / k)
+    return NVFP4_ERR_INVALID_VALUE;
+  if (mode != NVFP4_GLOBAL_COMPUTE && mode != NVFP4_GLOBAL_GIVEN)
+    return NVFP4_ERR_UNSUPPORTED;
+  if (out_dtype != NVFP4_DTYPE_F32 && out_dtype != NVFP4_DTYPE_BF16)
+    return NVFP4_ERR_UNSUPPORTED;
+  if (m > nvfp4::kMaxFusedRows || k % 128 != 0) return NVFP4_ERR_UNSUPPORTED;
+  if (!aligned(x_codes, 16) || !aligned(x_scales, 16) || !aligned(w_codes, 16) ||
+      !aligned(w_scales, 16) || !aligned(x_global, 4) || !aligned(w_global, 4) ||
+      !aligned(out, 4))
+    return NVFP4_ERR_MISALIGNED;
+  const int64_t es = x_dtype == NVFP4_DTYPE_F32 ? 4 : 2;
+  const int64_t os = out_dtype == NVFP4_DTYPE_F32 ? 4 : 2;
+  struct Range { const void* p; int64_t len; };
+  const Range in[] = {{x, ((m - 1) * ldx + k) * es}, {w_codes, n * (k / 2)},
+                      {w_scales, n * (k / 16)}, {w_global, 4}};
+  const Range outs[] = {{x_codes, m * (k / 2)}, {x_scales, m * (k / 16)},
+                        {x_global, 4}, {out, ((m - 1) * ldo + n) * os}};
+  for (int i = 0; i < 4; ++i) {
+    for (const Range& r : in)
+      if (overlap(outs[i].p, outs[i].len, r.p, r.len)) return NVFP4_ERR_INVALID_VALUE;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i].p, outs[i].len, outs[j].p, outs[j].len))
+        return NVFP4_ERR_INVALID_VALUE;
+  }
+  return status_of(nvfp4::launch_quantize_gemm(x, x_dtype, m, k, ldx, mode, x_codes, x_scales,
+                                               x_global, w_codes, w_scales, w_global, n, out,
+                                               out_dtype, ldo,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales,

@@ -26,11 +26,14 @@
 //     product unchanged and lets every lane read 16 contiguous bytes.
 //   * Epilogue: fp32 accumulator * (g_a g_b), optional gate, fp32 or bf16
 //     (round to nearest even) store.
+#include <hip/hip_cooperative_groups.h>
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <stdint.h>
 
 #include "internal.h"
+#include "quant_device.h"
 
 namespace nvfp4 {
 namespace {
@@ -853,19 +856,19 @@ __device__ __forceinline__ half8_t chunk_operand(const uint4& code, unsigned sc2
   return decode8(w, s);
 }
 
+// One workgroup's output tile `tile` (row-major over tiles_n tile columns);
+// a_g and b_g are the two global scales.
 template <int TMT, int TNT, int NWV, int KG, int CPG, int OUT, int EPI>
-__global__ void __launch_bounds__(NWV * 64)
-w4a4_gemm_skinny(const uint8_t* __restrict__ a_codes,
-                 const uint8_t* __restrict__ a_scales,
-                 const float* __restrict__ a_global, int64_t m,
-                 const uint8_t* __restrict__ b_codes,
-                 const uint8_t* __restrict__ b_scales,
-                 const float* __restrict__ b_global, int64_t n, int64_t k,
-                 void* __restrict__ out, int64_t ldo, int tiles_n, EpiArgs ep) {
+__device__ __forceinline__ void
+skinny_tile(int tile, const uint8_t* __restrict__ a_codes,
+            const uint8_t* __restrict__ a_scales, float a_g, int64_t m,
+            const uint8_t* __restrict__ b_codes,
+            const uint8_t* __restrict__ b_scales, float b_g, int64_t n, int64_t k,
+            void* __restrict__ out, int64_t ldo, int tiles_n, EpiArgs ep) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 31, h = lane >> 5;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.x / tiles_n) * (32 * TMT);
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x % tiles_n) * (32 * TNT);
+  const int64_t m0 = static_cast<int64_t>(tile / tiles_n) * (32 * TMT);
+  const int64_t n0 = static_cast<int64_t>(tile % tiles_n) * (32 * TNT);
   const int64_t kbytes = k / 2, kblocks = k / 16;
   const int64_t ngroups = k / (64 * CPG);
 
@@ -937,7 +940,7 @@ w4a4_gemm_skinny(const uint8_t* __restrict__ a_codes,
   // sum the waves' partial accumulators, one 32 x 32 tile at a time:
   // red[wave][e][lane]
   __shared__ float red[NWV][16][64];
-  const double gab = static_cast<double>(*a_global) * static_cast<double>(*b_global);
+  const double gab = static_cast<double>(a_g) * static_cast<double>(b_g);
 #pragma unroll
   for (int t = 0; t < TMT * TNT; ++t) {
     const int ti = t / TNT, tj = t % TNT;
@@ -949,7 +952,7 @@ w4a4_gemm_skinny(const uint8_t* __restrict__ a_codes,
 #pragma unroll 1
     for (int v0 = 0; v0 < 16 * 64; v0 += NWV * 64) {
       const int v = v0 + threadIdx.x;
-      if (NWV * 64 <= 16 * 64 || v < 16 * 64) {
+      if ((16 * 64) % (NWV * 64) == 0 || v < 16 * 64) {
         const int l = v & 63, e = v >> 6;
         float sum = red[0][e][l];
 #pragma unroll
@@ -982,6 +985,20 @@ w4a4_gemm_skinny(const uint8_t* __restrict__ a_codes,
   }
 }
 
+template <int TMT, int TNT, int NWV, int KG, int CPG, int OUT, int EPI>
+__global__ void __launch_bounds__(NWV * 64)
+w4a4_gemm_skinny(const uint8_t* __restrict__ a_codes,
+                 const uint8_t* __restrict__ a_scales,
+                 const float* __restrict__ a_global, int64_t m,
+                 const uint8_t* __restrict__ b_codes,
+                 const uint8_t* __restrict__ b_scales,
+                 const float* __restrict__ b_global, int64_t n, int64_t k,
+                 void* __restrict__ out, int64_t ldo, int tiles_n, EpiArgs ep) {
+  skinny_tile<TMT, TNT, NWV, KG, CPG, OUT, EPI>(blockIdx.x, a_codes, a_scales, *a_global, m,
+                                                b_codes, b_scales, *b_global, n, k, out, ldo,
+                                                tiles_n, ep);
+}
+
 template <int TMT, int TNT, int NWV, int KG, int OUT, int EPI>
 hipError_t launch_skinny(const uint8_t* a_codes, const uint8_t* a_scales,
                          const float* a_global, int64_t m,
@@ -1001,6 +1018,140 @@ hipError_t launch_skinny(const uint8_t* a_codes, const uint8_t* a_scales,
         a_codes, a_scales, a_global, m, b_codes, b_scales, b_global, n, k, out, ldo,
         static_cast<int>(tn), ep);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Small-M activation quantise + GEMM in one launch.  The limitations
+// section (한계) of the arxiv-wiki page on the paper puts a 2-4 % small-batch
+// decode loss on the quantisation of the activations; quantising X in the
+// GEMM's own launch removes the separate amax, finalise and quantise kernels.  One cooperative launch
+// (every workgroup resident at once) in two phases:
+//   1. the workgroups that own 16-element blocks of X (256 per workgroup)
+//      quantise them exactly as the quantisation kernel does; with a
+//      self-calibrated global each of them first takes max |x| over all of
+//      X itself (X has at most 64 rows), so no cross-workgroup reduction is
+//      needed, and workgroup 0 stores g;
+//   2. after one grid barrier (device-scope release and acquire) every
+//      workgroup runs skinny GEMM tiles on the codes just written, with the
+//      tile shape and K order that w4a4_gemm uses for the same m, so Y is
+//      bit-identical to quantise-then-w4a4_gemm.
+// Both phases stride over the grid, which the launcher caps at the number
+// of co-resident workgroups.
+
+template <int DTYPE, int TMT, int KG, int CPG, int OUT>
+__global__ void __launch_bounds__(256)
+w4a4_quantize_gemm(const uint8_t* __restrict__ x, int64_t m, int64_t k, int64_t ldx_bytes,
+                   int mode, uint8_t* __restrict__ x_codes, uint8_t* __restrict__ x_scales,
+                   float* __restrict__ x_global, const uint8_t* __restrict__ w_codes,
+                   const uint8_t* __restrict__ w_scales, const float* __restrict__ w_global,
+                   int64_t n, void* __restrict__ out, int64_t ldo, int tiles, int tiles_n) {
+  constexpr int kElemBytes = DTYPE == kDtypeF32 ? 4 : 2;
+  const int64_t kb = k / 16, nblocks = m * kb;
+  const bool contiguous = ldx_bytes == kb * 16 * kElemBytes;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  const int64_t first = static_cast<int64_t>(blockIdx.x) * 256;
+  if (first < nblocks) {   // uniform over the workgroup
+    float g;
+    if (mode == kModeCompute) {
+      unsigned mx = 0;
+      for (int64_t i = threadIdx.x; i < nblocks; i += 256) {
+        float v[16];
+        mx = max(mx, load_block<DTYPE>(block_src<DTYPE>(x, i, contiguous, kb, ldx_bytes), v));
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1)
+        mx = max(mx, static_cast<unsigned>(__shfl_xor(static_cast<int>(mx), off)));
+      __shared__ unsigned part[4];
+      if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = mx;
+      __syncthreads();
+      mx = max(max(part[0], part[1]), max(part[2], part[3]));
+      g = global_from_amax(__uint_as_float(mx));
+      if (blockIdx.x == 0 && threadIdx.x == 0) *x_global = g;
+    } else {
+      g = *x_global;
+    }
+    bool g_ok;
+    const float inv6g = recip_6g(g, &g_ok);
+    __shared__ __attribute__((aligned(16))) float lds_rows[256 * kRowFloats];
+    float* row = lds_rows + threadIdx.x * kRowFloats;
+    for (int64_t b = first + threadIdx.x; b < nblocks; b += stride)
+      quantize_one<DTYPE>(block_src<DTYPE>(x, b, contiguous, kb, ldx_bytes), b, g, inv6g, g_ok,
+                          x_codes, x_scales, row);
+  }
+  // every code, scale and the global of X are written and visible
+  // device-wide after the barrier
+  cooperative_groups::this_grid().sync();
+  const float a_g = __hip_atomic_load(x_global, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const float b_g = *w_global;
+  for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    if (tile != static_cast<int>(blockIdx.x)) __syncthreads();   // LDS of the previous tile is free
+    skinny_tile<TMT, 1, 4, KG, CPG, OUT, kEpiNone>(tile, x_codes, x_scales, a_g, m, w_codes,
+                                                  w_scales, b_g, n, k, out, ldo, tiles_n,
+                                                  EpiArgs{});
+  }
+}
+
+// Co-resident workgroups of `kernel` on the current device (0 if the
+// runtime cannot tell), cached per device in the caller's `cache`.
+template <typename Kernel>
+int resident_workgroups(Kernel kernel, int block, std::atomic<int> (&cache)[64]) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  const int total = per_cu * cus;
+  if (dev < 64) cache[dev].store(total, std::memory_order_relaxed);
+  return total;
+}
+
+template <int DTYPE, int TMT, int KG, int CPG, int OUT>
+hipError_t launch_quantize_gemm_cfg(const void* x, int64_t m, int64_t k, int64_t ldx,
+                                    int mode, uint8_t* x_codes, uint8_t* x_scales,
+                                    float* x_global, const uint8_t* w_codes,
+                                    const uint8_t* w_scales, const float* w_global, int64_t n,
+                                    void* out, int64_t ldo, hipStream_t stream) {
+  auto kernel = w4a4_quantize_gemm<DTYPE, TMT, KG, CPG, OUT>;
+  const int64_t tm = (m + 32 * TMT - 1) / (32 * TMT), tn = (n + 31) / 32;
+  const int64_t tiles = tm * tn;
+  const int64_t qwgs = (m * (k / 16) + 255) / 256;
+  static std::atomic<int> resident_cache[64];   // one per kernel instance
+  const int resident = resident_workgroups(kernel, 256, resident_cache);
+  if (resident < 1) return hipErrorCooperativeLaunchTooLarge;
+  if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  int64_t grid = tiles > qwgs ? tiles : qwgs;
+  if (grid > resident) grid = resident;
+  const uint8_t* xb = static_cast<const uint8_t*>(x);
+  int64_t ldx_bytes = ldx * (DTYPE == kDtypeF32 ? 4 : 2);
+  int tiles_i = static_cast<int>(tiles), tn_i = static_cast<int>(tn);
+  void* args[] = {&xb, &m, &k, &ldx_bytes, &mode, &x_codes, &x_scales, &x_global, &w_codes,
+                  &w_scales, &w_global, &n, &out, &ldo, &tiles_i, &tn_i};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kernel),
+                                    dim3(static_cast<unsigned>(grid)), dim3(256), args, 0,
+                                    stream);
+}
+
+template <int DTYPE, int OUT>
+hipError_t launch_quantize_gemm_k(const void* x, int64_t m, int64_t k, int64_t ldx, int mode,
+                                  uint8_t* x_codes, uint8_t* x_scales, float* x_global,
+                                  const uint8_t* w_codes, const uint8_t* w_scales,
+                                  const float* w_global, int64_t n, void* out, int64_t ldo,
+                                  hipStream_t stream) {
+  // the same tile shapes and K groups as the skinny dispatch of w4a4_gemm
+#define NVFP4_QG_ARGS x, m, k, ldx, mode, x_codes, x_scales, x_global, w_codes, w_scales, \
+                      w_global, n, out, ldo, stream
+  if (m <= 32) {
+    if (k % 256 == 0) return launch_quantize_gemm_cfg<DTYPE, 1, 1, 4, OUT>(NVFP4_QG_ARGS);
+    return launch_quantize_gemm_cfg<DTYPE, 1, 2, 2, OUT>(NVFP4_QG_ARGS);
+  }
+  if (k % 256 == 0) return launch_quantize_gemm_cfg<DTYPE, 2, 1, 4, OUT>(NVFP4_QG_ARGS);
+  return launch_quantize_gemm_cfg<DTYPE, 2, 2, 2, OUT>(NVFP4_QG_ARGS);
+#undef NVFP4_QG_ARGS
 }
 
 template <int WM, int WN, int TM, int TN, bool ALIGNED, int OUT, int EPI>
@@ -1081,6 +1232,22 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
   if (epilogue == kEpiBeta) return dispatch_align<1, kEpiBeta>(NVFP4_GEMM_ARGS);
   return dispatch_align<1, kEpiNone>(NVFP4_GEMM_ARGS);
 #undef NVFP4_GEMM_ARGS
+}
+
+hipError_t launch_quantize_gemm(const void* x, int x_dtype, int64_t m, int64_t k, int64_t ldx,
+                                int mode, uint8_t* x_codes, uint8_t* x_scales,
+                                float* x_global, const uint8_t* w_codes,
+                                const uint8_t* w_scales, const float* w_global, int64_t n,
+                                void* out, int out_dtype, int64_t ldo, hipStream_t stream) {
+#define NVFP4_QG_ARGS x, m, k, ldx, mode, x_codes, x_scales, x_global, w_codes, w_scales, \
+                      w_global, n, out, ldo, stream
+  if (x_dtype == kDtypeF32) {
+    if (out_dtype == kOutF32) return launch_quantize_gemm_k<0, 0>(NVFP4_QG_ARGS);
+    return launch_quantize_gemm_k<0, 1>(NVFP4_QG_ARGS);
+  }
+  if (out_dtype == kOutF32) return launch_quantize_gemm_k<1, 0>(NVFP4_QG_ARGS);
+  return launch_quantize_gemm_k<1, 1>(NVFP4_QG_ARGS);
+#undef NVFP4_QG_ARGS
 }
 
 hipError_t launch_gdn_gates(const uint8_t* x_codes, const uint8_t* x_scales,

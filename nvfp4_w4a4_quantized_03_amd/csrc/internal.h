@@ -29,6 +29,16 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                        void* out, int out_dtype, int64_t ldo, int epilogue,
                        hipStream_t stream);
 
+// Small-M (m <= 64) activation quantise + W4A4 GEMM in one cooperative
+// launch (gemm.hip); k % 128 == 0 and 16-byte aligned code and scale arrays
+// are checked by the caller.
+constexpr int64_t kMaxFusedRows = 64;
+hipError_t launch_quantize_gemm(const void* x, int x_dtype, int64_t m, int64_t k, int64_t ldx,
+                                int mode, uint8_t* x_codes, uint8_t* x_scales,
+                                float* x_global, const uint8_t* w_codes,
+                                const uint8_t* w_scales, const float* w_global, int64_t n,
+                                void* out, int out_dtype, int64_t ldo, hipStream_t stream);
+
 // Gate pair of a fused b|a projection (gemm.hip); k % 128 == 0, 16-byte
 // aligned scale arrays and n_beta + n_alpha <= 256 are checked by the caller.
 constexpr int64_t kMaxGateCols = 256;

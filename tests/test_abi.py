@@ -37,10 +37,10 @@ def test_exports_every_declared_symbol(lib):
                           "nvfp4_dequantize", "fp8_kv_amax_update",
                           "fp8_kv_scale_from_amax", "fp8_kv_cast",
                           "nvfp4_error_stats", "nvfp4_status_string",
-                          "nvfp4_abi_version"}
+                          "nvfp4_abi_version", "w4a4_gemm_quantize_a"}
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.nvfp4_abi_version() == 2
+    assert lib.nvfp4_abi_version() == 3
     for s in range(6):
         assert lib.nvfp4_status_string(s)
 
@@ -117,6 +117,36 @@ def test_gemm_validation(lib):
     assert gm(lib, out=P + 0x600002) == MISALIGNED
     assert gm(lib, out=P + 0x300010) == INVALID       # out overlaps b codes
     assert gm(lib, out=P + 0x200000 - 8) == INVALID   # out covers a_global
+
+
+def fq(lib, x=P, dt=1, m=4, k=256, ldx=256, xc=P + 0x100000, xs=P + 0x200000,
+       xg=P + 0x300000, mode=0, wc=P + 0x400000, ws=P + 0x500000,
+       wg=P + 0x600000, n=8, out=P + 0x700000, od=1, ldo=8):
+    return lib.w4a4_gemm_quantize_a(x, dt, m, k, ldx, xc, xs, xg, mode, wc, ws,
+                                    wg, n, out, od, ldo, None)
+
+
+def test_gemm_quantize_a_validation(lib):
+    for kw in ("x", "xc", "xs", "xg", "wc", "ws", "wg", "out"):
+        assert fq(lib, **{kw: None}) == INVALID, kw
+    assert fq(lib, m=0) == INVALID
+    assert fq(lib, n=0) == INVALID
+    assert fq(lib, k=8, ldx=8) == INVALID
+    assert fq(lib, ldx=128) == INVALID                # ldx < k
+    assert fq(lib, ldo=4) == INVALID                  # ldo < n
+    assert fq(lib, dt=5) == UNSUPPORTED
+    assert fq(lib, mode=2) == UNSUPPORTED
+    assert fq(lib, od=3) == UNSUPPORTED
+    assert fq(lib, m=65) == UNSUPPORTED               # not a small-M shape
+    assert fq(lib, k=272, ldx=272) == UNSUPPORTED     # k % 128 != 0
+    assert fq(lib, x=P + 8) == MISALIGNED
+    assert fq(lib, xs=P + 0x200008) == MISALIGNED
+    assert fq(lib, ws=P + 0x500004) == MISALIGNED
+    assert fq(lib, out=P + 0x700002) == MISALIGNED
+    assert fq(lib, xc=P + 0x40) == INVALID            # codes overlap x
+    assert fq(lib, out=P + 0x400010) == INVALID       # out overlaps w codes
+    assert fq(lib, xg=P + 0x200004) == INVALID        # global inside scales
+    assert fq(lib, out=P + 0x100000 + 0x100) == INVALID   # out overlaps codes
 
 
 def gg(lib, xc=P, xs=P + 0x100000, xg=P + 0x200000, m=4, wc=P + 0x300000,
