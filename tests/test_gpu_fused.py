@@ -151,3 +151,23 @@ def test_fused_zero_activations():
     assert host(qx.global_scale)[0] == 0
     assert not host(qx.codes).any() and not host(qx.scales).any()
     assert not _bits(y).any()
+
+
+@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+def test_fused_strided_activations(xdt):
+    """X as a column slice of a wider tensor (row stride 400 > k = 384): the
+    quantise phase takes the strided block addressing."""
+    m, n, k, ld = 20, 150, 384, 400
+    rng = np.random.default_rng(31)
+    full = rng.standard_normal((m, ld)).astype(np.float32)
+    wv = (rng.standard_normal((n, k)) * 0.05).astype(np.float32)
+    qw = nv.quantize(up(wv, None, "f32"))
+    if xdt == "bf16":
+        fv, fd = bf16_dev(full)
+    else:
+        fv, fd = full, up(full, None, "f32")
+    xv, xd = fv[:, :k], fd[:, :k]
+    _say("fused strided", xdt)
+    for gt in (None, torch.tensor([np.float32(oracle.global_scale(xv) * 2)],
+                                  dtype=torch.float32, device=DEV)):
+        _check_against_separate_and_oracle(xv, xd, wv, qw, gt, torch.float32)
