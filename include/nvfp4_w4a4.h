@@ -28,7 +28,9 @@
  *
  * Conventions for every call:
  *   - All buffers are device memory owned by the caller; the library
- *     allocates nothing and keeps no state between calls.
+ *     allocates nothing.  Its only state between calls is a per-device
+ *     cache of the co-resident workgroup count of the fused call's kernels
+ *     (w4a4_gemm_quantize_a).
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls validate
  *     their arguments on the host, enqueue kernels and return without
  *     synchronising.  A kernel fault is reported by the next synchronising

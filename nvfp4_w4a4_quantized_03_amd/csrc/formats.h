@@ -1,5 +1,5 @@
-// Device helpers for the OCP E4M3 block-scale format shared by the
-// quantisation and harmonisation kernels.
+// Device helpers for the OCP E4M3 format, shared by every kernel that
+// reads or writes E4M3 block scales or FP8 KV codes.
 //
 // E4M3 is the block-scale format of NVFP4 (explainer page
 // "論文解説: Gated DeltaNet はなぜ4bit量子化に耐えるのか", section 前提1); read as
