@@ -233,16 +233,23 @@ def other_workloads(nv, synth, dev, stream, reps=10):
     # dequantise (fake-quant half) to bf16 and per-row error statistics
     yb = torch.empty((32768, 5120), dtype=torch.bfloat16, device=dev)
     t_d = _time(lambda: nv.dequantize(q, torch.bfloat16, out=yb), reps, stream)
+    del yb
+    yf = torch.empty((32768, 5120), dtype=torch.float32, device=dev)
+    t_f = _time(lambda: nv.dequantize(q, torch.float32, out=yf), reps, stream)
+    del yf
     t_e = _time(lambda: nv.error_stats(xv, q), reps, stream)
     elems = 32768 * 5120
     out["dequantize_error_stats_32768x5120"] = {
         "dequantize_bf16_us": t_d,
         "dequantize_gbps_2.5625B_per_elem": elems * 2.5625 / t_d / 1e3,
         "dequantize_frac_hbm_peak": elems * 2.5625 / t_d / 1e3 / PEAK_HBM_GBPS,
+        "dequantize_f32_us": t_f,
+        "dequantize_f32_gbps_4.5625B_per_elem": elems * 4.5625 / t_f / 1e3,
+        "dequantize_f32_frac_hbm_peak": elems * 4.5625 / t_f / 1e3 / PEAK_HBM_GBPS,
         "error_stats_us": t_e,
         "error_stats_gbps_2.5625B_per_elem": elems * 2.5625 / t_e / 1e3,
         "error_stats_frac_hbm_peak": elems * 2.5625 / t_e / 1e3 / PEAK_HBM_GBPS}
-    del yb, q, xv
+    del q, xv
     # decode projection 32 x 10240 x 5120: activation quantisation + GEMM as
     # two library calls and as the one-launch fused call, with COMPUTE
     # (self-calibrated) and GIVEN globals.  Direct C-ABI calls with

@@ -6,9 +6,10 @@
 // has at most 6 significant bits and is exact in binary32; times the
 // binary32 global the exact value has at most 30, so:
 //   * binary32 output: one IEEE multiply, a single rounding;
-//   * bfloat16 output: the exact product rounded to binary32 with
-//     round-to-odd and then to bfloat16 to nearest even, which equals one
-//     rounding of the exact value (binary32 keeps 16 more bits).
+//   * bfloat16 output: the binary32 product rounded to bfloat16 to nearest
+//     even, with the exact product deciding where the binary32 value lies
+//     exactly on a bfloat16 midpoint; that equals one rounding of the exact
+//     value.
 // Error statistics (the A4 / W4 error percentages and max/RMS of the
 // input statistics on the arxiv-wiki page, section 접근 방법): per row,
 // in float64, sum x^2, sum (x - x_hat)^2 and max |x|.
@@ -47,35 +48,44 @@ __device__ __forceinline__ unsigned short bf16_rne_bits(float f) {
   return static_cast<unsigned short>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-// Nearest-even bfloat16 of the exact product v * g (v = e2m1 * e4m3, exact):
-// round to binary32 with round-to-odd, then to bfloat16.  For a product of
-// normal magnitude the binary32 residual fma(v, g, -f) is exact, so its sign
-// says whether f was rounded away from zero; near the subnormal range the
-// exact product is formed in float64 instead.
+// Nearest-even bfloat16 of the exact product v * g (v = e2m1 * e4m3, exact).
+// f = fl32(v * g) is one correct rounding; rounding f once more to bfloat16
+// differs from one rounding of the exact product only where f lies exactly
+// on a bfloat16 midpoint (low 16 bits 0x8000): a midpoint is itself a
+// binary32 value, so rounding to binary32 can reach one but never cross it.
+// There the exact product decides: larger in magnitude than f rounds away
+// from zero, smaller toward zero, equal keeps the tie (to even).  The
+// residual fma(v, g, -f) is exact for products of normal magnitude; near the
+// subnormal range the product is formed in float64 (exact: v * g has at
+// most 30 significant bits).
 __device__ __forceinline__ unsigned short bf16_of_product(float v, float g) {
-  float f = v * g;
-  if (__builtin_fabsf(f) >= 0x1p-100f) {
-    const float e = __builtin_fmaf(v, g, -f);   // exact - f, exactly
-    if (e != 0.0f) {
-      unsigned b = __float_as_uint(f);
-      if ((e < 0.0f) != (f < 0.0f)) b -= 1u;     // f was rounded away from zero
-      f = __uint_as_float(b | 1u);
+  const float f = v * g;
+  unsigned u = __float_as_uint(f);
+  if ((u & 0xFFFFu) == 0x8000u) {
+    int dir = 0;   // sign of |exact| - |f|
+    if (__builtin_fabsf(f) >= 0x1p-100f) {
+      const float e = __builtin_fmaf(v, g, -f);   // exact - f, exactly
+      if (e != 0.0f) dir = ((e > 0.0f) == (f > 0.0f)) ? 1 : -1;
+    } else {
+      const double p = static_cast<double>(v) * static_cast<double>(g);   // exact
+      const double fd = static_cast<double>(f);
+      if (p != fd) dir = __builtin_fabs(p) > __builtin_fabs(fd) ? 1 : -1;
     }
-    return bf16_rne_bits(f);
+    u = dir > 0 ? u + 1u : dir < 0 ? u - 1u : u;   // off the midpoint, or the tie
   }
-  const double p = static_cast<double>(v) * static_cast<double>(g);   // exact
-  f = static_cast<float>(p);
-  if (static_cast<double>(f) != p) {
-    unsigned b = __float_as_uint(f);
-    if (__builtin_fabs(static_cast<double>(f)) > __builtin_fabs(p)) b -= 1u;   // toward zero
-    f = __uint_as_float(b | 1u);
-  }
-  return bf16_rne_bits(f);
+  return bf16_rne_bits(__uint_as_float(u));
 }
 
-// One 16-element block per lane: 8 code bytes + 1 scale byte in, 16 values
-// out (64 or 32 contiguous bytes per lane, so a wave's stores coalesce;
-// non-temporal, as the output is a stream).
+// Lanes per block: every lane stores one 16-byte piece of the output (four
+// binary32 or eight bfloat16 values), so that a wave's non-temporal store
+// covers 1 KiB contiguously.  With one lane per block (several stores per
+// lane, 32 or 64 bytes apart) the streaming stores ran 1.5x (bf16) to 8x
+// (fp32) slower.
+template <int OUT>
+constexpr int kLanesPerBlock = OUT == kOutF32 ? 4 : 2;
+
+// 8 code bytes + 1 scale byte in, 16 values out per block, over
+// kLanesPerBlock lanes; non-temporal stores, as the output is a stream.
 template <int OUT>
 __global__ void __launch_bounds__(256)
 dequantize_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
@@ -83,34 +93,42 @@ dequantize_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__
                   void* __restrict__ out, int64_t ldo) {
   const float g = *global;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t b = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-       b < nblocks; b += stride) {
-    const uint2 c = reinterpret_cast<const uint2*>(codes)[b];
-    const float sc = e4m3_f32(scales[b]);
-    float v[16];
-    decode_block(c, sc, v);
-    const int64_t row = b / kb, col = (b - row * kb) * 16;
-    if constexpr (OUT == kOutF32) {
-      typedef float f32x4 __attribute__((ext_vector_type(4)));
-      f32x4* o = reinterpret_cast<f32x4*>(static_cast<float*>(out) + row * ldo + col);
+  if constexpr (OUT == kOutF32) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+         t < nblocks * 4; t += stride) {
+      const int64_t b = t >> 2;
+      const unsigned c = reinterpret_cast<const unsigned short*>(codes)[t];   // 4 codes
+      const float sc = e4m3_f32(scales[b]);
+      const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
+      const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1);
+      const int64_t row = b / kb, col = (b - row * kb) * 16 + (t & 3) * 4;
+      // (e2m1 * e4m3) is exact; times g it is rounded once
+      const f32x4 o = {(p0[0] * sc) * g, (p0[1] * sc) * g, (p1[0] * sc) * g, (p1[1] * sc) * g};
+      __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(static_cast<float*>(out) + row * ldo + col));
+    }
+  } else {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+         t < nblocks * 2; t += stride) {
+      const int64_t b = t >> 1;
+      const unsigned c = reinterpret_cast<const unsigned*>(codes)[t];   // 8 codes
+      const float sc = e4m3_f32(scales[b]);
+      unsigned w[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 t = {v[4 * q] * g, v[4 * q + 1] * g, v[4 * q + 2] * g, v[4 * q + 3] * g};
-        __builtin_nontemporal_store(t, o + q);
+      for (int j = 0; j < 4; ++j) {
+        const f32x2 p = j == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0)
+                      : j == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1)
+                      : j == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2)
+                               : __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
+        w[j] = static_cast<unsigned>(bf16_of_product(p[0] * sc, g)) |
+               (static_cast<unsigned>(bf16_of_product(p[1] * sc, g)) << 16);
       }
-    } else {
-      unsigned w[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const unsigned lo = bf16_of_product(v[2 * q], g);
-        const unsigned hi = bf16_of_product(v[2 * q + 1], g);
-        w[q] = lo | (hi << 16);
-      }
-      typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-      u32x4* o = reinterpret_cast<u32x4*>(static_cast<unsigned short*>(out) + row * ldo + col);
-      const u32x4 t0 = {w[0], w[1], w[2], w[3]}, t1 = {w[4], w[5], w[6], w[7]};
-      __builtin_nontemporal_store(t0, o);
-      __builtin_nontemporal_store(t1, o + 1);
+      const int64_t row = b / kb, col = (b - row * kb) * 16 + (t & 1) * 8;
+      const u32x4 o = {w[0], w[1], w[2], w[3]};
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(static_cast<unsigned short*>(out) + row * ldo + col));
     }
   }
 }
@@ -187,7 +205,8 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales,
                              void* out, int out_dtype, int64_t ldo,
                              hipStream_t stream) {
   const int64_t kb = k / 16, nblocks = rows * kb;
-  const int64_t want = (nblocks + 255) / 256;
+  const int64_t lanes = nblocks * (out_dtype == kOutF32 ? kLanesPerBlock<0> : kLanesPerBlock<1>);
+  const int64_t want = (lanes + 255) / 256;
   const unsigned grid = static_cast<unsigned>(want < 0x7FFFFFFF ? want : 0x7FFFFFFF);
   if (out_dtype == kOutF32)
     dequantize_kernel<0><<<grid, 256, 0, stream>>>(codes, scales, global, nblocks, kb, out, ldo);

@@ -59,6 +59,59 @@ def test_dequantize_strided_output():
     assert np.all(got[:, :32] == 7.0) and np.all(got[:, 288:] == 7.0)
 
 
+def test_dequantize_strided_bf16_output():
+    codes, scales, g, q = _random_nvfp4(40, 256, 0.0625, 4)
+    big = torch.zeros((40, 320), dtype=torch.bfloat16, device=DEV)
+    nv.dequantize(q, torch.bfloat16, out=big[:, 48:304])
+    got = host(big.view(torch.int16)).view(np.uint16)
+    assert np.array_equal(got[:, 48:304], oracle.dequantize_bf16(codes, scales, g))
+    assert not got[:, :48].any() and not got[:, 304:].any()
+
+
+def _bf16_midpoint_cases(count, seed):
+    """(code nibble, scale byte, g) with fp32(e2m1 * e4m3 * g) exactly on a
+    bfloat16 midpoint while the exact product is not: the only products for
+    which rounding the binary32 value again to bfloat16 gives another
+    result than one rounding of the exact value."""
+    rng = np.random.default_rng(seed)
+    e2m1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    e4m3 = oracle.e4m3_decode_table()
+    cases = []
+    while len(cases) < count:
+        code, sbyte = int(rng.integers(1, 8)), int(rng.integers(1, 127))
+        v = e2m1[code] * float(e4m3[sbyte])
+        target = np.array([(int(rng.integers(0x2000, 0x5000)) << 16) | 0x8000],
+                          dtype=np.uint32).view(np.float32)[0]
+        g = np.float32(float(target) / v)
+        if not np.isfinite(g) or g <= 0:
+            continue
+        exact = v * float(g)                    # exact in float64
+        f = np.float32(exact)
+        if (int(f.view(np.uint32)) & 0xFFFF) == 0x8000 and float(f) != exact:
+            cases.append((code, sbyte, g))
+    return cases
+
+
+def test_dequantize_bf16_at_binary32_midpoints():
+    """Products whose binary32 rounding lands on a bfloat16 midpoint: the
+    device must round the exact product, not the binary32 value."""
+    naive_wrong = 0
+    for i, (code, sbyte, g) in enumerate(_bf16_midpoint_cases(48, 11)):
+        codes = np.zeros((1, 16), dtype=np.uint8)
+        codes[0, :8] = code | (code << 4)                  # block 0: +v
+        codes[0, 8:] = (code | 8) | ((code | 8) << 4)      # block 1: -v
+        scales = np.array([[sbyte, sbyte]], dtype=np.uint8)
+        q = nv.NVFP4(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV),
+                     torch.tensor([g], dtype=torch.float32, device=DEV))
+        want = oracle.dequantize_bf16(codes, scales, g)
+        got = host(nv.dequantize(q, torch.bfloat16).view(torch.int16)).view(np.uint16)
+        assert np.array_equal(got, want), (i, code, sbyte, float(g))
+        twice = oracle.bf16_rne_from_f64(
+            oracle.dequantize(codes, scales, g).astype(np.float32).astype(np.float64))[1]
+        naive_wrong += int(np.any(twice != want))
+    assert naive_wrong > 0   # the cases do separate the two roundings
+
+
 def test_fake_quantize_round_trip():
     rng = np.random.default_rng(11)
     x = (rng.standard_normal((64, 512)) * 2).astype(np.float32)
