@@ -93,6 +93,7 @@ dequantize_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__
                   void* __restrict__ out, int64_t ldo) {
   const float g = *global;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  const bool flat = ldo == kb * 16;   // rows back to back: no division per lane
   if constexpr (OUT == kOutF32) {
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -103,10 +104,14 @@ dequantize_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__
       const float sc = e4m3_f32(scales[b]);
       const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
       const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1);
-      const int64_t row = b / kb, col = (b - row * kb) * 16 + (t & 3) * 4;
+      int64_t dst = t * 4;
+      if (!flat) {
+        const int64_t row = b / kb;
+        dst = row * ldo + (b - row * kb) * 16 + (t & 3) * 4;
+      }
       // (e2m1 * e4m3) is exact; times g it is rounded once
       const f32x4 o = {(p0[0] * sc) * g, (p0[1] * sc) * g, (p1[0] * sc) * g, (p1[1] * sc) * g};
-      __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(static_cast<float*>(out) + row * ldo + col));
+      __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(static_cast<float*>(out) + dst));
     }
   } else {
     typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -126,9 +131,13 @@ dequantize_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__
         w[j] = static_cast<unsigned>(bf16_of_product(p[0] * sc, g)) |
                (static_cast<unsigned>(bf16_of_product(p[1] * sc, g)) << 16);
       }
-      const int64_t row = b / kb, col = (b - row * kb) * 16 + (t & 1) * 8;
+      int64_t dst = t * 8;
+      if (!flat) {
+        const int64_t row = b / kb;
+        dst = row * ldo + (b - row * kb) * 16 + (t & 1) * 8;
+      }
       const u32x4 o = {w[0], w[1], w[2], w[3]};
-      __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(static_cast<unsigned short*>(out) + row * ldo + col));
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(static_cast<unsigned short*>(out) + dst));
     }
   }
 }

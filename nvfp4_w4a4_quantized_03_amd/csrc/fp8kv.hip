@@ -48,10 +48,14 @@ __device__ __forceinline__ void load16(const uint8_t* src, float* v) {
   }
 }
 
+// Source of 16-element group b; `flat` (rows stored back to back) skips the
+// 64-bit division by the groups per row.
 template <int DTYPE>
 __device__ __forceinline__ const uint8_t* group_src(const uint8_t* x, int64_t b,
-                                                    int64_t kg, int64_t ldx_bytes) {
+                                                    int64_t kg, int64_t ldx_bytes,
+                                                    bool flat) {
   constexpr int64_t kBytes = 16 * (DTYPE == kDtypeF32 ? 4 : 2);
+  if (flat) return x + b * kBytes;
   const int64_t row = b / kg;
   return x + row * ldx_bytes + (b - row * kg) * kBytes;
 }
@@ -62,11 +66,12 @@ template <int DTYPE>
 __global__ void __launch_bounds__(256)
 kv_amax_kernel(const uint8_t* __restrict__ x, int64_t ngroups, int64_t kg,
                int64_t ldx_bytes, unsigned* __restrict__ amax_bits) {
+  const bool flat = ldx_bytes == kg * 16 * (DTYPE == kDtypeF32 ? 4 : 2);
   unsigned mx = 0u;
   for (int64_t b = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
        b < ngroups; b += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     float v[16];
-    load16<DTYPE>(group_src<DTYPE>(x, b, kg, ldx_bytes), v);
+    load16<DTYPE>(group_src<DTYPE>(x, b, kg, ldx_bytes, flat), v);
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = max(mx, __float_as_uint(v[i]) & 0x7FFFFFFFu);
   }
@@ -102,11 +107,49 @@ __device__ __forceinline__ unsigned kv_code(float ax, float r_lo, float r_hi, do
   return e4m3_settle(c, static_cast<double>(ax), s);
 }
 
+// Codes of one 16-element group, stored as one non-temporal 16-byte piece
+// (the codes are a stream; a wave's stores cover 1 KiB).  `normal`: s within
+// [2^-100, 2^100], where the bracketed conversion applies; otherwise every
+// code is settled in float64 (or is 0 when s == 0).  Both flags are uniform,
+// so the per-element work has no branch on them.
+template <int DTYPE>
+__device__ __forceinline__ void kv_cast_group(const uint8_t* src, uint8_t* dst, bool zero,
+                                              bool normal, float r_lo, float r_hi,
+                                              double sd) {
+  float v[16];
+  load16<DTYPE>(src, v);
+  unsigned w[4] = {0u, 0u, 0u, 0u};
+  if (normal) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const unsigned c = kv_code(__builtin_fabsf(v[i]), r_lo, r_hi, sd) |
+                         ((__float_as_uint(v[i]) >> 24) & 0x80u);
+      w[i >> 2] |= c << (8 * (i & 3));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const double ax = static_cast<double>(__builtin_fabsf(v[i]));
+      const unsigned m = zero ? 0u : e4m3_settle(e4m3_candidate(ax / sd), ax, sd);
+      const unsigned c = m | ((__float_as_uint(v[i]) >> 24) & 0x80u);
+      w[i >> 2] |= c << (8 * (i & 3));
+    }
+  }
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 o = {w[0], w[1], w[2], w[3]};
+  __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(dst));
+}
+
+// One 16-element group per lane.  A grid that covers every group of a flat
+// (rows back to back) tensor, the launcher's normal case, takes a
+// straight-line body; the grid-stride loop serves strided tensors and grids
+// capped at the launch limit.
 template <int DTYPE>
 __global__ void __launch_bounds__(256)
 kv_cast_kernel(const uint8_t* __restrict__ x, int64_t ngroups, int64_t kg,
                int64_t ldx_bytes, const float* __restrict__ scale,
                uint8_t* __restrict__ out, int64_t ldo) {
+  constexpr int64_t kBytes = 16 * (DTYPE == kDtypeF32 ? 4 : 2);
   const float s = *scale;
   const double sd = static_cast<double>(s);
   const bool zero = !(s > 0.0f);
@@ -117,28 +160,18 @@ kv_cast_kernel(const uint8_t* __restrict__ x, int64_t ngroups, int64_t kg,
     r_lo = r * (1.0f - 0x1p-18f);
     r_hi = r * (1.0f + 0x1p-18f);
   }
-  for (int64_t b = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-       b < ngroups; b += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    float v[16];
-    load16<DTYPE>(group_src<DTYPE>(x, b, kg, ldx_bytes), v);
-    unsigned w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float ax = __builtin_fabsf(v[i]);
-      unsigned c = 0u;
-      if (!zero) {
-        if (normal)
-          c = kv_code(ax, r_lo, r_hi, sd);
-        else
-          c = e4m3_settle(e4m3_candidate(static_cast<double>(ax) / sd),
-                          static_cast<double>(ax), sd);
-      }
-      c |= (__float_as_uint(v[i]) >> 24) & 0x80u;
-      w[i >> 2] |= c << (8 * (i & 3));
-    }
+  const bool flat = ldx_bytes == kg * kBytes && ldo == kg * 16;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  const int64_t b0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (flat && stride >= ngroups) {
+    if (b0 < ngroups)
+      kv_cast_group<DTYPE>(x + b0 * kBytes, out + b0 * 16, zero, normal, r_lo, r_hi, sd);
+    return;
+  }
+  for (int64_t b = b0; b < ngroups; b += stride) {
     const int64_t row = b / kg;
-    *reinterpret_cast<uint4*>(out + row * ldo + (b - row * kg) * 16) =
-        make_uint4(w[0], w[1], w[2], w[3]);
+    kv_cast_group<DTYPE>(x + row * ldx_bytes + (b - row * kg) * kBytes,
+                         out + row * ldo + (b - row * kg) * 16, zero, normal, r_lo, r_hi, sd);
   }
 }
 
@@ -153,7 +186,9 @@ hipError_t launch_kv_amax_update(const void* x, int x_dtype, int64_t rows, int64
                                  int64_t ldx, float* amax, hipStream_t stream) {
   const int64_t kg = k / 16, ngroups = rows * kg;
   const int64_t esize = x_dtype == kDtypeF32 ? 4 : 2;
-  const unsigned grid = grid_for(ngroups) < 2048 ? grid_for(ngroups) : 2048;
+  // at most 512 workgroups, each ending with one atomic on the same word
+  // (2048 measured twice as slow on a 32768 x 1024 slab)
+  const unsigned grid = grid_for(ngroups) < 512 ? grid_for(ngroups) : 512;
   const uint8_t* xb = static_cast<const uint8_t*>(x);
   unsigned* bits = reinterpret_cast<unsigned*>(amax);
   if (x_dtype == kDtypeF32)
