@@ -756,6 +756,51 @@ w4a4_gemm_pipelined(const uint8_t* __restrict__ a_codes,
   // with non-temporal stores, so that it does not linger there as dirty
   // lines for the next kernel to write back
   const double gab = static_cast<double>(*a_global) * static_cast<double>(*b_global);
+  if constexpr (OUT != kOutF32) {
+    // bf16, a full tile, a 16-byte aligned output with whole 16-byte pieces
+    // per row: each 32-row slice of the wave's tiles goes through the first
+    // ring slot (idle once every wave is past the main loop) so that a lane
+    // stores 16 contiguous bytes, 4 rows x 256 bytes per wave store; the
+    // accumulator layout (2 bytes per lane, 64-byte row pieces) made the
+    // stores cost about 2% more of the kernel
+    constexpr int kStride = TN * 32 * 2 + 16;   // staged row bytes, padded off the bank period
+    static_assert(NW * 32 * kStride <= kSlotBytes, "staging fits one ring slot");
+    const bool whole = m0 + BM <= m && n0 + BN <= n &&
+                       reinterpret_cast<uintptr_t>(out) % 16 == 0 && ldo % 8 == 0;
+    if (whole) {
+      __syncthreads();
+      uint8_t* stage = s0 + wave * 32 * kStride;
+      const int c = lane & 31, h = lane >> 5;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int r = 8 * (e >> 2) + 4 * h + (e & 3);
+            const float y = epilogue<EPI>(static_cast<float>(static_cast<double>(acc[i][j][e]) * gab));
+            *reinterpret_cast<unsigned short*>(stage + r * kStride + (j * 32 + c) * 2) =
+                f32_to_bf16_rne(y);
+          }
+        __syncthreads();
+        constexpr int kPieces = 32 * TN * 4;   // 16-byte pieces of the slice
+        static_assert(kPieces % 64 == 0, "whole pieces per lane");
+#pragma unroll
+        for (int it = 0; it < kPieces / 64; ++it) {
+          const int q = it * 64 + lane;
+          const int r = q / (TN * 4), cb = (q % (TN * 4)) * 16;
+          const uint4 v = *reinterpret_cast<const uint4*>(stage + r * kStride + cb);
+          typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+          const u32x4 w = {v.x, v.y, v.z, v.w};
+          __builtin_nontemporal_store(
+              w, reinterpret_cast<u32x4*>(static_cast<unsigned short*>(out) +
+                                          (m0 + arow + i * 32 + r) * ldo + n0 + brow + cb / 2));
+        }
+        __syncthreads();   // the slice is read before the next one is written
+      }
+      return;
+    }
+  }
   const int col_l = lane & 31, row_l = (lane >> 5) * 4;
 #pragma unroll
   for (int i = 0; i < TM; ++i)

@@ -373,6 +373,32 @@ def test_gemm_strided_output():
     assert np.all(got[:, :8] == 7.0) and np.all(got[:, 32:] == 7.0)
 
 
+@pytest.mark.parametrize("m,n", [(512, 512), (600, 520)])
+@pytest.mark.parametrize("col0,ld", [(8, 528), (2, 528), (8, 532)])
+def test_gemm_bf16_tiles_into_wider_output(m, n, col0, ld):
+    """bf16 output of the pipelined kernel (m, n > 64) written into a wider
+    buffer: full tiles at a 16-byte aligned start with a row stride of whole
+    16-byte pieces go through the LDS-staged store; a 4-byte aligned start
+    or another stride, and partial tiles, take the per-element store.  The
+    rest of the buffer stays untouched."""
+    k = 256
+    rng = np.random.default_rng(m + n + col0 + ld)
+    xv = rng.standard_normal((m, k)).astype(np.float32)
+    wv = (rng.standard_normal((n, k)) * 0.05).astype(np.float32)
+    _say("gemm bf16 wide output", m, n, col0, ld)
+    qa = nv.quantize(up(xv, None, "f32"))
+    qb = nv.quantize(up(wv, None, "f32"))
+    ref = oracle.gemm_exact_int(*oracle.quantize(xv), *oracle.quantize(wv))
+    for epi, f in (("none", lambda r: r), ("alpha", oracle.gate_alpha),
+                   ("beta", oracle.gate_beta)):
+        big = torch.full((m, ld), 3.0, dtype=torch.bfloat16, device=DEV)
+        view = big[:, col0:col0 + n]
+        nv.gemm(qa, qb, out_dtype=torch.bfloat16, epilogue=epi, out=view)
+        check_bf16_within_one_ulp(view, f(ref))
+        got = host(big.float())
+        assert np.all(got[:, :col0] == 3.0) and np.all(got[:, col0 + n:] == 3.0)
+
+
 def _sampled_gemm_check(xv, qa, wv, qb, rows, cols, y_dev, out_dtype,
                         epilogue="none"):
     ca, sa, ga = oracle.quantize(xv[rows], g=oracle.global_scale(xv))
