@@ -609,7 +609,8 @@ __device__ __forceinline__ void pipe_stage(
   constexpr int kIssues = kIssuesA + kIssuesB;
   // Every stage issues the same loads, so the wait below is one count.  Past
   // the last stage the fill repeats stage nk - 1 into the slot just freed,
-  // which no later stage reads.  A's loads go out with the first k-step's
+  // which no later stage reads.  The slot filled here (stage kt - 1's) was
+  // last read in the first half of stage kt - 1, before that stage's barrier.  A's loads go out with the first k-step's
   // MFMAs and B's with the fourth's: spreading them keeps the memory queue
   // from stalling the in-order MFMA issue (~3% faster than one burst).
   const int fs = kt + NS - 1 < nk ? kt + NS - 1 : nk - 1;
@@ -617,6 +618,16 @@ __device__ __forceinline__ void pipe_stage(
   la.issue(k0, ring.a[fill_slot], ring.sa[fill_slot], wave);
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
+    if (half == 1) {
+      // The second half starts by reading the first half of stage kt + 1,
+      // whose rows other waves loaded: this wave waits for its own loads of
+      // stage kt + 1 (those of stages kt + 2 .. kt + NS - 1 may stay in
+      // flight), and the barrier then covers everyone's.  Placed here rather
+      // than at the end of the stage, the one barrier per stage also orders
+      // this stage's reads of its slot before the next stage refills it.
+      __builtin_amdgcn_s_waitcnt(kVmcntKeepOf((NS - 2) * kIssues));
+      stage_barrier();
+    }
     // fragments of the following half-stage (the next stage's first half
     // when this is the second half; a resident slot is read even after the
     // last stage, and never used)
@@ -653,10 +664,6 @@ __device__ __forceinline__ void pipe_stage(
     fa = na;
     fb = nb;
   }
-  // stage kt + 1 must have landed before the barrier; the fills of stages
-  // kt + 2 .. kt + NS - 1 may stay in flight
-  __builtin_amdgcn_s_waitcnt(kVmcntKeepOf((NS - 2) * kIssues));
-  stage_barrier();
 }
 
 template <int WM, int WN, int TM, int TN, int OUT, int EPI>
@@ -718,20 +725,17 @@ w4a4_gemm_pipelined(const uint8_t* __restrict__ a_codes,
   PipeLoader<BN, NW> lb;
   la.init(a_codes, a_scales, m0, m, k, wave, lane);
   lb.init(b_codes, b_scales, n0, n, k, wave, lane);
-  // prologue: stages 0 .. NS-2 into slots 0 .. NS-2
+  // prologue: stages 0 .. NS-2 into slots 0 .. NS-2 (past the last stage,
+  // stage nk - 1 again, which only the unused prefetch after it reads); stage
+  // 0 must have landed, the later ones may stay in flight
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st) {
-    if (st < nk) {
-      la.issue(static_cast<int64_t>(st) * kBK, ring.a[st], ring.sa[st], wave);
-      lb.issue(static_cast<int64_t>(st) * kBK, ring.b[st], ring.sb[st], wave);
-    }
+    const int64_t k0 = static_cast<int64_t>(st < nk ? st : nk - 1) * kBK;
+    la.issue(k0, ring.a[st], ring.sa[st], wave);
+    lb.issue(k0, ring.b[st], ring.sb[st], wave);
   }
-  // stage 0 must have landed; stages 1 .. NS-2 may stay in flight
   constexpr int kIssues = PipeLoader<BM, NW>::kIssues + PipeLoader<BN, NW>::kIssues;
-  if (nk >= NS - 1)
-    __builtin_amdgcn_s_waitcnt(kVmcntKeepOf((NS - 2) * kIssues));
-  else
-    __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_waitcnt(kVmcntKeepOf((NS - 2) * kIssues));
   stage_barrier();
 
   HalfFrags<TM> fa;

@@ -316,7 +316,8 @@ def test_gemm_tiny_exact(out_dtype):
                                    (40, 1000, 512), (1000, 50, 256),
                                    (7, 777, 384), (513, 257, 640),
                                    (300, 200, 128), (130, 300, 256),
-                                   (200, 129, 384), (33, 700, 640)])
+                                   (200, 129, 384), (33, 700, 640),
+                                   (136, 264, 768), (130, 200, 1664)])
 def test_gemm_ragged_shapes(m, n, k):
     rng = np.random.default_rng(m * 31 + n * 7 + k)
     xv = rng.standard_normal((m, k)).astype(np.float32)
