@@ -510,6 +510,36 @@ def test_gemm_prefill_and_decode_full_size():
                         torch.bfloat16)
 
 
+def test_gemm_repeated_launches_bit_identical():
+    """Every wave of a pipelined-GEMM workgroup fills rows that the others
+    read, so a missing wait or barrier shows as run-to-run differences:
+    back-to-back launches (full-size prefill, and a small-K shape whose
+    tiles are mostly prologue and epilogue) must give identical bits."""
+    xv, xb, xt = workload(5, "x")
+    wv, wb, wt = workload(5, "w")
+    qa = nv.quantize(up(xv, xb, xt))
+    qb = nv.quantize(up(wv, wb, wt))
+    for od, reps in ((torch.bfloat16, 12), (torch.float32, 4)):
+        _say("gemm repeat prefill", od, reps)
+        ref = nv.gemm(qa, qb, out_dtype=od)
+        out = torch.empty_like(ref)
+        ibits = torch.int16 if od == torch.bfloat16 else torch.int32
+        for i in range(reps):
+            nv.gemm(qa, qb, out_dtype=od, out=out)
+            assert torch.equal(out.view(ibits), ref.view(ibits)), i
+        del ref, out
+    rng = np.random.default_rng(12)
+    m, n, k = 4160, 4224, 640
+    qa = nv.quantize(up(rng.standard_normal((m, k)).astype(np.float32), None, "f32"))
+    qb = nv.quantize(up(rng.standard_normal((n, k)).astype(np.float32), None, "f32"))
+    _say("gemm repeat", m, n, k)
+    ref = nv.gemm(qa, qb, out_dtype=torch.bfloat16)
+    out = torch.empty_like(ref)
+    for i in range(50):
+        nv.gemm(qa, qb, out_dtype=torch.bfloat16, out=out)
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), i
+
+
 def test_calls_on_a_side_stream():
     rng = np.random.default_rng(8)
     xv = rng.standard_normal((64, 512)).astype(np.float32)
