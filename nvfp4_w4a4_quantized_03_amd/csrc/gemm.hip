@@ -390,10 +390,12 @@ w4a4_gemm_kernel(const uint8_t* __restrict__ a_codes,
 //   decoded while the 16 MFMAs of the current k-step issue.  Each stage
 //   issues the same loads (past the last stage they repeat it into the slot
 //   just freed), A's with the first k-step's MFMAs and B's with the
-//   fourth's; one wait that leaves the NS - 2 newest fills in flight and one
-//   barrier per stage keep the ring ordered: stage kt + NS - 1 goes into the
-//   slot of stage kt - 1, which every wave finished before the barrier that
-//   closed stage kt - 1.
+//   fourth's.  One wait (the fills of the NS - 2 newest stages stay in
+//   flight) and one barrier per stage, between its two halves, keep the ring
+//   ordered: stage kt + 1, loaded by every wave, has landed before the second
+//   half of stage kt reads its first half; and stage kt + NS - 1 goes into
+//   the slot of stage kt - 1, whose last reads came before the mid-stage
+//   barrier of stage kt - 1.
 // * Rows past m or n load a clamped (valid) row; their outputs are never
 //   stored.  Offsets within a tile are 32-bit, so the launcher takes this
 //   kernel only for k <= 2^22.
