@@ -338,7 +338,8 @@ w4a4_gemm_kernel(const uint8_t* __restrict__ a_codes,
 
   // Epilogue.  32x32 accumulator layout: lane l holds column l % 32 and, for
   // element e, row 8 (e / 4) + 4 (l / 32) + e % 4.
-  // g_a g_b is exact in float64; one rounding to binary32 per output
+  // g_a g_b is exact in float64; the product with the accumulator is formed
+  // in float64 and rounded to binary32
   const double gab = static_cast<double>(*a_global) * static_cast<double>(*b_global);
   const int col_l = lane & 31, row_l = (lane >> 5) * 4;
 #pragma unroll
