@@ -253,6 +253,29 @@ def test_harmonize_every_scale_byte():
         assert np.array_equal(host(d), ref), ratios
 
 
+@pytest.mark.parametrize("scale", [1.0, 2.0 ** 110, 2.0 ** -110])
+@pytest.mark.parametrize("aligned", [True, False])
+def test_harmonize_ragged_modules(scale, aligned):
+    """Rows of 5 scale bytes (k = 80) and modules of 1-3 rows, so a lane's
+    bytes straddle module boundaries; a module with global 0 and two with
+    the shared maximum; the array at an odd address (byte-wise path) or
+    aligned; shared globals beyond 2^100 or below 2^-100 (float64 path)."""
+    rng = np.random.default_rng(41)
+    rows_per = [1, 3, 1, 2, 1, 4, 2]
+    offs = [0] + list(np.cumsum(rows_per))
+    k = 80
+    sc = rng.integers(0, 0x7F, (offs[-1], k // 16)).astype(np.uint8)
+    gs = [np.float32(v * scale) for v in (0.3, 1.7, 0.0, 1.7, 1e-3, 0.999, 1.25)]
+    ref, gstar = oracle.harmonize(sc, offs, gs)
+    buf = torch.empty(sc.size + 1, dtype=torch.uint8, device=DEV)
+    d = (buf[:sc.size] if aligned else buf[1:]).view(sc.shape)
+    d.copy_(torch.from_numpy(sc))
+    _say("harmonize ragged", scale, aligned)
+    out = nv.harmonize_group(d, k, offs, torch.tensor(gs, dtype=torch.float32, device=DEV))
+    assert host(out)[0] == gstar
+    assert np.array_equal(host(d), ref)
+
+
 def test_harmonize_fused_group_full_size():
     """Three modules with different per-module globals quantised into row
     slices of one fused buffer, then harmonised (the fused qkv|z style
