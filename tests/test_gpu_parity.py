@@ -276,6 +276,22 @@ def test_harmonize_ragged_modules(scale, aligned):
     assert np.array_equal(host(d), ref)
 
 
+def test_harmonize_most_modules():
+    """64 modules (the most the call takes) of one row of 5 scale bytes
+    each, with distinct globals: a boundary falls inside almost every
+    lane's 4 bytes."""
+    rng = np.random.default_rng(43)
+    n_mod, k = 64, 80
+    offs = list(range(n_mod + 1))
+    sc = rng.integers(0, 0x7F, (n_mod, k // 16)).astype(np.uint8)
+    gs = [np.float32(v) for v in rng.uniform(0.01, 2.0, n_mod)]
+    ref, gstar = oracle.harmonize(sc, offs, gs)
+    d = torch.from_numpy(sc.copy()).to(DEV)
+    out = nv.harmonize_group(d, k, offs, torch.tensor(gs, dtype=torch.float32, device=DEV))
+    assert host(out)[0] == gstar
+    assert np.array_equal(host(d), ref)
+
+
 def test_harmonize_fused_group_full_size():
     """Three modules with different per-module globals quantised into row
     slices of one fused buffer, then harmonised (the fused qkv|z style
