@@ -1,13 +1,18 @@
-"""Seeded random sweep of W4A4 GEMM shapes through the C ABI, against the
-exact oracle product.  The shapes fall on every kernel the library picks
-(skinny tiles for m or n up to 64 with either K-group size, the pipelined
-kernel, the staged kernel for ragged k or unaligned scale arrays), with
-ragged edges, both output types, the gate epilogues and strided outputs.
+"""Seeded random sweeps through the C ABI, against the oracle.
 
-Bars as in test_gpu_parity: fp32 output within relative Frobenius error
-1e-5 of the exact product (gated: of the gate of it); bf16 output within
-one bf16 ulp of the exact value rounded to bf16; output columns past n
-untouched.
+GEMM: shapes that fall on every kernel the library picks (skinny tiles for
+m or n up to 64 with either K-group size, the pipelined kernel, the staged
+kernel for ragged k or unaligned scale arrays), with ragged edges, both
+output types, the gate epilogues and strided outputs.  Bars as in
+test_gpu_parity: fp32 output within relative Frobenius error 1e-5 of the
+exact product (gated: of the gate of it); bf16 output within one bf16 ulp
+of the exact value rounded to bf16; output columns past n untouched.
+
+Quantise -> dequantise -> error statistics: random shapes, row strides,
+input types, global modes and value mixes (normal with outlier channels,
+log-uniform magnitudes over 1e-20..1e20, sparse, values near E2M1
+midpoints).  Codes, scales, globals and dequantised values bit-exact; the
+statistics' maxima exact and sums within 1e-12 relative.
 """
 import numpy as np
 import pytest
@@ -15,6 +20,7 @@ import torch
 
 import nvfp4_w4a4_quantized_03_amd as nv
 import oracle
+import synth
 from test_gpu_parity import DEV, TOL, check_bf16_within_one_ulp, host, rel_frob, up
 
 pytestmark = pytest.mark.gpu
@@ -90,3 +96,73 @@ def test_gemm_random_shape(case):
         check_bf16_within_one_ulp(y, ref)
     if pad:
         assert torch.all(big[:, n:] == -3.0)
+
+
+# ------------------------------------------------- quantise / dequantise
+
+def _values(rng, rows, k, kind):
+    """Seeded inputs of several magnitude mixes."""
+    if kind == "normal":
+        x = rng.standard_normal((rows, k))
+        x[:, rng.integers(0, k, max(1, k // 100))] *= 60.0        # outlier channels
+    elif kind == "loguniform":
+        x = np.exp(rng.uniform(np.log(1e-20), np.log(1e20), (rows, k)))
+        x *= rng.choice([-1.0, 1.0], (rows, k))
+    elif kind == "sparse":
+        x = rng.standard_normal((rows, k)) * (rng.random((rows, k)) < 0.1)
+    else:                                                           # "grid": near E2M1 midpoints
+        mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+        x = rng.choice(mids, (rows, k)) * np.exp2(rng.integers(-3, 4, (rows, 1)))
+        x *= 1.0 + rng.choice([0.0, 2.0 ** -20, -(2.0 ** -20)], (rows, k))
+    return x.astype(np.float32)
+
+
+def _qcases(count, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        out.append(dict(rows=int(rng.integers(1, 300)), k=16 * int(rng.integers(1, 200)),
+                        pad=int(rng.choice([0, 0, 8, 40])),
+                        dtype=("f32", "bf16")[int(rng.integers(0, 2))],
+                        mode=("compute", "given")[int(rng.integers(0, 2))],
+                        kind=("normal", "loguniform", "sparse", "grid")[int(rng.integers(0, 4))],
+                        seed=int(rng.integers(0, 2**31))))
+    return out
+
+
+@pytest.mark.parametrize("case", _qcases(40, 20261209),
+                         ids=lambda c: "%(rows)dx%(k)d+%(pad)d-%(dtype)s-%(mode)s-%(kind)s" % c)
+def test_quantize_dequantize_random(case):
+    """Quantise (codes, scales and global bit-exact with the oracle),
+    then dequantise (each output one rounding of the exact value) and the
+    error statistics of the same tensors, on a strided input."""
+    _say(case)
+    rng = np.random.default_rng(case["seed"])
+    rows, k, pad = case["rows"], case["k"], case["pad"]
+    full = _values(rng, rows, k + pad, case["kind"])
+    if case["dtype"] == "bf16":
+        bits = synth.bf16_bits_from_f32(full)
+        full = synth.f32_from_bf16_bits(bits)
+        fd = torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+    else:
+        fd = up(full, None, "f32")
+    x, xd = full[:, :k], fd[:, :k]
+    g_ref = oracle.global_scale(x)
+    gt = None
+    if case["mode"] == "given":
+        g_ref = np.float32(g_ref * np.float32(rng.uniform(0.5, 2.0)))
+        gt = torch.tensor([g_ref], dtype=torch.float32, device=DEV)
+    q = nv.quantize(xd, global_scale=gt)
+    c_ref, s_ref, _ = oracle.quantize(x, g=g_ref)
+    assert np.float32(host(q.global_scale)[0]).view(np.uint32) == np.float32(g_ref).view(np.uint32)
+    assert np.array_equal(host(q.scales), s_ref)
+    assert np.array_equal(host(q.codes), c_ref)
+    f32 = host(nv.dequantize(q, torch.float32))
+    assert np.array_equal(f32.view(np.uint32), oracle.dequantize_f32(c_ref, s_ref, g_ref).view(np.uint32))
+    b16 = host(nv.dequantize(q, torch.bfloat16).view(torch.int16)).view(np.uint16)
+    assert np.array_equal(b16, oracle.dequantize_bf16(c_ref, s_ref, g_ref))
+    st = host(nv.error_stats(xd, q))
+    ref = oracle.error_stats(x, c_ref, s_ref, g_ref)
+    assert np.array_equal(st[:, 2], ref[:, 2])
+    for col in (0, 1):
+        assert np.all(np.abs(st[:, col] - ref[:, col]) <= 1e-12 * np.abs(ref[:, col]) + 1e-300)
