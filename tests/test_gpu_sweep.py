@@ -13,6 +13,11 @@ input types, global modes and value mixes (normal with outlier channels,
 log-uniform magnitudes over 1e-20..1e20, sparse, values near E2M1
 midpoints).  Codes, scales, globals and dequantised values bit-exact; the
 statistics' maxima exact and sums within 1e-12 relative.
+
+FP8 KV cache: calibration over several strided slabs and the cast into a
+strided output, amax, scale and every code bit-exact.  GDN gate pair:
+random token counts, head counts and per-head parameters, gates within
+1e-5 relative Frobenius error of the oracle's gates of the exact product.
 """
 import numpy as np
 import pytest
@@ -166,3 +171,85 @@ def test_quantize_dequantize_random(case):
     assert np.array_equal(st[:, 2], ref[:, 2])
     for col in (0, 1):
         assert np.all(np.abs(st[:, col] - ref[:, col]) <= 1e-12 * np.abs(ref[:, col]) + 1e-300)
+
+
+# ------------------------------------------------------------- FP8 KV cache
+
+def _kvcases(count, seed):
+    rng = np.random.default_rng(seed)
+    return [dict(rows=int(rng.integers(1, 300)), k=16 * int(rng.integers(1, 160)),
+                 pad=int(rng.choice([0, 0, 16, 48])), opad=int(rng.choice([0, 16])),
+                 dtype=("f32", "bf16")[int(rng.integers(0, 2))],
+                 kind=("normal", "loguniform", "sparse")[int(rng.integers(0, 3))],
+                 parts=int(rng.integers(1, 4)), seed=int(rng.integers(0, 2**31)))
+            for _ in range(count)]
+
+
+@pytest.mark.parametrize("case", _kvcases(24, 20261210),
+                         ids=lambda c: "%(rows)dx%(k)d+%(pad)d-%(dtype)s-%(kind)s-%(parts)d" % c)
+def test_fp8_kv_random(case):
+    """Calibration over 1-3 strided slabs (running amax and scale
+    bit-exact), then the cast of a fresh strided slab into a strided
+    output (every code bit-exact, padding untouched)."""
+    _say(case)
+    rng = np.random.default_rng(case["seed"])
+    rows, k, pad, opad = case["rows"], case["k"], case["pad"], case["opad"]
+
+    def slab():
+        full = _values(rng, rows, k + pad, case["kind"])
+        if case["dtype"] == "bf16":
+            bits = synth.bf16_bits_from_f32(full)
+            full = synth.f32_from_bf16_bits(bits)
+            fd = torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+        else:
+            fd = up(full, None, "f32")
+        return full[:, :k], fd[:, :k]
+    parts = [slab() for _ in range(case["parts"])]
+    scale, amax = nv.fp8_kv_calibrate([d for _, d in parts])
+    a_ref = oracle.kv_amax([v for v, _ in parts])
+    s_ref = oracle.kv_scale(a_ref)
+    assert np.float32(host(amax)[0]).view(np.uint32) == a_ref.view(np.uint32)
+    assert np.float32(host(scale)[0]).view(np.uint32) == s_ref.view(np.uint32)
+    xv, xd = slab()
+    big = torch.full((rows, k + opad), 0xA5, dtype=torch.uint8, device=DEV)
+    nv.fp8_kv_cast(xd, scale, out=big[:, :k])
+    got = host(big)
+    assert np.array_equal(got[:, :k], oracle.kv_cast(xv, s_ref))
+    assert np.all(got[:, k:] == 0xA5)
+
+
+# ----------------------------------------------------------- GDN gate pair
+
+def _gcases(count, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        nb = int(rng.choice([0, int(rng.integers(1, 129))]))
+        na = int(rng.integers(1 if nb == 0 else 0, 129))
+        out.append(dict(m=int(rng.integers(1, 600)), nb=nb, na=na,
+                        k=128 * int(rng.integers(1, 24)), seed=int(rng.integers(0, 2**31))))
+    return out
+
+
+@pytest.mark.parametrize("case", _gcases(16, 20261211),
+                         ids=lambda c: "%(m)dx(%(nb)d+%(na)d)x%(k)d" % c)
+def test_gdn_gates_random(case):
+    """The gate pair of a fused b|a projection on random shapes and
+    per-head parameters, against the oracle's gates of the exact product."""
+    _say(case)
+    rng = np.random.default_rng(case["seed"])
+    m, nb, na, k = case["m"], case["nb"], case["na"], case["k"]
+    xv = rng.standard_normal((m, k)).astype(np.float32)
+    wv = (rng.standard_normal((nb + na, k)) * 0.05).astype(np.float32)
+    a_log = rng.uniform(-2.0, 1.5, na).astype(np.float32)
+    dt = rng.uniform(-3.0, 3.0, na).astype(np.float32)
+    qa = nv.quantize(up(xv, None, "f32"))
+    qb = nv.quantize(up(wv, None, "f32"))
+    y = oracle.gemm_exact_int(*oracle.quantize(xv), *oracle.quantize(wv))
+    beta_ref, alpha_ref = oracle.gdn_gates(y, nb, a_log, dt)
+    beta, alpha = nv.gdn_gates(qa, qb, nb, torch.from_numpy(a_log).to(DEV),
+                               torch.from_numpy(dt).to(DEV))
+    if nb:
+        assert rel_frob(host(beta).astype(np.float64), beta_ref) <= TOL
+    if na:
+        assert rel_frob(host(alpha).astype(np.float64), alpha_ref) <= TOL
