@@ -18,6 +18,8 @@ FP8 KV cache: calibration over several strided slabs and the cast into a
 strided output, amax, scale and every code bit-exact.  GDN gate pair:
 random token counts, head counts and per-head parameters, gates within
 1e-5 relative Frobenius error of the oracle's gates of the exact product.
+Fused small-M quantise + GEMM: random m <= 64, n, k, input types and
+global modes, bit-identical to the two separate calls.
 """
 import numpy as np
 import pytest
@@ -253,3 +255,55 @@ def test_gdn_gates_random(case):
         assert rel_frob(host(beta).astype(np.float64), beta_ref) <= TOL
     if na:
         assert rel_frob(host(alpha).astype(np.float64), alpha_ref) <= TOL
+
+
+# ------------------------------------------ fused small-M quantise + GEMM
+
+def _fcases(count, seed):
+    rng = np.random.default_rng(seed)
+    return [dict(m=int(rng.integers(1, 65)), n=int(rng.integers(1, 3000)),
+                 k=128 * int(rng.integers(1, 20)),
+                 dtype=("f32", "bf16")[int(rng.integers(0, 2))],
+                 mode=("compute", "given")[int(rng.integers(0, 2))],
+                 out=("f32", "bf16")[int(rng.integers(0, 2))],
+                 seed=int(rng.integers(0, 2**31)))
+            for _ in range(count)]
+
+
+@pytest.mark.parametrize("case", _fcases(16, 20261212),
+                         ids=lambda c: "%(m)dx%(n)dx%(k)d-%(dtype)s-%(mode)s-%(out)s" % c)
+def test_fused_quantize_gemm_random(case):
+    """One-launch quantise + GEMM on random small-M shapes: X's NVFP4 form
+    and Y bit-identical to the two separate calls, Y against the exact
+    product of the oracle's quantisation."""
+    _say(case)
+    rng = np.random.default_rng(case["seed"])
+    m, n, k = case["m"], case["n"], case["k"]
+    xv = rng.standard_normal((m, k)).astype(np.float32)
+    xv[:, rng.integers(0, k, 2)] *= np.float32(40.0)
+    wv = (rng.standard_normal((n, k)) * 0.05).astype(np.float32)
+    if case["dtype"] == "bf16":
+        bits = synth.bf16_bits_from_f32(xv)
+        xv = synth.f32_from_bf16_bits(bits)
+        xd = torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+    else:
+        xd = up(xv, None, "f32")
+    qw = nv.quantize(up(wv, None, "f32"))
+    g_ref = oracle.global_scale(xv)
+    gt = None
+    if case["mode"] == "given":
+        g_ref = np.float32(g_ref * np.float32(1.5))
+        gt = torch.tensor([g_ref], dtype=torch.float32, device=DEV)
+    od = torch.float32 if case["out"] == "f32" else torch.bfloat16
+    qx, y = nv.gemm_quantize_a(xd, qw, global_scale=gt, out_dtype=od)
+    qs = nv.quantize(xd, global_scale=gt)
+    for a, b in ((qx.codes, qs.codes), (qx.scales, qs.scales), (qx.global_scale, qs.global_scale)):
+        assert torch.equal(a, b)
+    ys = nv.gemm(qs, qw, out_dtype=od)
+    ib = torch.int16 if od == torch.bfloat16 else torch.int32
+    assert torch.equal(y.view(ib), ys.view(ib)), "fused Y differs from quantize + gemm"
+    ref = oracle.gemm_exact_int(*oracle.quantize(xv, g=g_ref), *oracle.quantize(wv))
+    if od == torch.float32:
+        assert rel_frob(host(y).astype(np.float64), ref) <= TOL
+    else:
+        check_bf16_within_one_ulp(y, ref)
