@@ -72,15 +72,16 @@ def measured_traffic(kernel_file, per_launch_units):
 
 
 def cpu_baseline():
-    """The oracle, as it stands, on a bounded sample of the step's work:
-    quantize 8192 rows of X (numpy, one core) and the W4A4 GEMM of 2048 of
-    those rows against 4096 weight rows (float64 BLAS on the decoded
-    operands, all BLAS threads).  Scaled to the whole step's flops."""
+    """The oracle, as it stands, on a bounded sample of the step's work
+    (about 10 s of CPU time): quantize 16384 rows of X (numpy, one core)
+    and the W4A4 GEMM of 8192 of those rows against all 10240 weight rows
+    (float64 BLAS on the decoded operands, all BLAS threads).  Scaled to
+    the whole step's flops."""
     import oracle
     import synth
     from threadpoolctl import threadpool_info
-    GM, GN = 2048, 4096
-    xv, _, _ = synth.workload_tensor(WORKLOAD, "x", row_ids=np.arange(8192))
+    GQ, GM, GN = 16384, 8192, N
+    xv, _, _ = synth.workload_tensor(WORKLOAD, "x", row_ids=np.arange(GQ))
     wv, _, _ = synth.workload_tensor(WORKLOAD, "w", row_ids=np.arange(GN))
     g = np.float32(0.25)
     t0 = time.perf_counter()
@@ -102,11 +103,11 @@ def cpu_baseline():
         "unit": "TFLOP/s",
         "cores": int(blas),
         "kind": "oracle",
-        "sample": ("oracle.quantize of X rows 0..8191 (%.2f s, 1 core) and "
-                   "oracle.gemm_f64 2048x4096x5120 (%.2f s, %d BLAS threads), "
+        "sample": ("oracle.quantize of X rows 0..%d (%.2f s, 1 core) and "
+                   "oracle.gemm_f64 %dx%dx%d (%.2f s, %d BLAS threads), "
                    "scaled per element / per flop to one step "
                    "(quantize 32800x5120 + GEMM 32800x10240x5120)"
-                   % (tq, tg, blas)),
+                   % (GQ - 1, tq, GM, GN, K, tg, blas)),
         "quantize_gbps": xv.size * 2.5625 / tq / 1e9,
         "gemm_tflops": 2.0 * GM * GN * K / tg / 1e12,
     }
