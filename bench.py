@@ -71,23 +71,35 @@ def measured_traffic(kernel_file, per_launch_units):
     return float(byt.group(1))
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline():
     """The oracle, as it stands, on a bounded sample of the step's work
     (about 10 s of CPU time): quantize 16384 rows of X (numpy, one core)
     and the W4A4 GEMM of 8192 of those rows against all 10240 weight rows
-    (float64 BLAS on the decoded operands, all BLAS threads).  Scaled to
-    the whole step's flops."""
+    (float64 BLAS on the decoded operands, all BLAS threads).  Each tensor
+    gets its own self-calibrated global, as the GPU step's given globals
+    are.  Scaled to the whole step's flops."""
     import oracle
     import synth
     from threadpoolctl import threadpool_info
     GQ, GM, GN = 16384, 8192, N
     xv, _, _ = synth.workload_tensor(WORKLOAD, "x", row_ids=np.arange(GQ))
     wv, _, _ = synth.workload_tensor(WORKLOAD, "w", row_ids=np.arange(GN))
-    g = np.float32(0.25)
+    gx = oracle.global_scale(xv)
     t0 = time.perf_counter()
-    qa = oracle.quantize(xv, g=g)
+    qa = oracle.quantize(xv, g=gx)
     tq = time.perf_counter() - t0
-    qb = oracle.quantize(wv, g=g)
+    qb = oracle.quantize(wv)
     qa = tuple(t[:GM] if t.ndim else t for t in qa)
     t0 = time.perf_counter()
     oracle.gemm_f64(*qa, *qb)
@@ -96,20 +108,31 @@ def cpu_baseline():
     q_elems = (M + M_DEC) * K
     t_step = tq / xv.size * q_elems + tg / (2.0 * GM * GN * K) * \
         (2.0 * (M + M_DEC) * N * K)
-    blas = max([d.get("num_threads", 1) for d in threadpool_info()
-                if d.get("user_api") == "blas"] or [1])
+    blas = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+    blas_threads = max([d.get("num_threads", 1) for d in blas] or [1])
+    blas_lib = ", ".join(sorted({"%s %s (%s)" % (d.get("internal_api", "?"),
+                                                 d.get("version", "?"),
+                                                 os.path.basename(d.get("filepath", "?")))
+                                 for d in blas})) or "unknown"
+    host_cores = len(os.sched_getaffinity(0))
     return {
         "value": 2.0 * (M + M_DEC) * N * K / t_step / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(blas),
+        "cores": int(blas_threads),
         "kind": "oracle",
         "sample": ("oracle.quantize of X rows 0..%d (%.2f s, 1 core) and "
                    "oracle.gemm_f64 %dx%dx%d (%.2f s, %d BLAS threads), "
                    "scaled per element / per flop to one step "
                    "(quantize 32800x5120 + GEMM 32800x10240x5120)"
-                   % (GQ - 1, tq, GM, GN, K, tg, blas)),
+                   % (GQ - 1, tq, GM, GN, K, tg, blas_threads)),
         "quantize_gbps": xv.size * 2.5625 / tq / 1e9,
+        "quantize_cores": 1,
         "gemm_tflops": 2.0 * GM * GN * K / tg / 1e12,
+        "gemm_cores": int(blas_threads),
+        "host_cores": host_cores,
+        "cpu_model": _cpu_model(),
+        "blas": blas_lib,
+        "blas_threads": int(blas_threads),
     }
 
 

@@ -140,13 +140,14 @@ int nvfp4_harmonize_group(uint8_t* scales, int64_t k,
  * beta = sigmoid(y).
  *
  *   a_codes, a_scales, a_global  activations A [m][k] in the layout above
- *                                (codes 16-byte aligned).
+ *                                (codes and scales 16-byte aligned, else
+ *                                MISALIGNED).
  *   b_codes, b_scales, b_global  weights B [n][k] (K-major, the same
- *                                layout; codes 16-byte aligned).
- *   m, n, k      m, n >= 1, k >= 16, k % 16 == 0.
- *                Scale arrays may have any alignment; the fast kernels
- *                need k % 128 == 0 and both scale arrays 16-byte aligned
- *                (other calls take a slower kernel with byte-wise guards).
+ *                                layout and alignment).
+ *   m, n, k      m, n >= 1, k >= 16, k % 16 == 0.  k % 128 == 0 takes the
+ *                whole-stage kernels; other k (rows whose code and scale
+ *                bytes do not fill 16-byte pieces) a kernel that guards
+ *                each piece.
  *   out          device, [m][ldo] of out_dtype (F32 or BF16), ldo >= n;
  *                4-byte aligned.  Must not overlap the inputs.
  *   epilogue     w4a4_epilogue, applied in fp32 before the store.

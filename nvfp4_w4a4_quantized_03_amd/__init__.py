@@ -103,9 +103,25 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _device_tensor(t, name):
+def _device_tensor(t, name, dtype=None, numel=None, device=None):
+    """Refuse anything but a GPU tensor (optionally of one dtype, element
+    count and device) before any pointer reaches the library: a host or
+    mistyped buffer would otherwise be read or written by a kernel."""
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError("%s must be a torch tensor on a GPU" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, not %s" % (name, dtype, t.dtype))
+    if numel is not None and t.numel() != numel:
+        raise ValueError("%s must hold %d element(s), not %d"
+                         % (name, numel, t.numel()))
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, the other operands on %s"
+                         % (name, t.device, device))
+
+
+def _global_tensor(t, name, device):
+    """A float32 device scalar (one element) on the operands' device."""
+    _device_tensor(t, name, torch.float32, 1, device)
 
 
 def quantize(x, global_scale=None, out=None):
@@ -129,22 +145,24 @@ def quantize(x, global_scale=None, out=None):
     rows, k = x.shape
     # a one-row tensor's row stride is arbitrary (numpy/torch may report 0)
     ldx = x.stride(0) if rows > 1 else k
-    if out is None:
-        codes = torch.empty((rows, k // 2), dtype=torch.uint8, device=x.device)
-        scales = torch.empty((rows, k // 16), dtype=torch.uint8,
-                             device=x.device)
-    else:
+    # every caller-supplied buffer is checked before anything is allocated
+    if global_scale is not None:
+        _global_tensor(global_scale, "global_scale", x.device)
+    if out is not None:
         codes, scales = out
+        _device_tensor(codes, "out codes", torch.uint8, device=x.device)
+        _device_tensor(scales, "out scales", torch.uint8, device=x.device)
         if codes.shape != (rows, k // 2) or scales.shape != (rows, k // 16) \
                 or not codes.is_contiguous() or not scales.is_contiguous():
             raise ValueError("out buffers have the wrong shape or layout")
+    else:
+        codes = torch.empty((rows, k // 2), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((rows, k // 16), dtype=torch.uint8,
+                             device=x.device)
     if global_scale is None:
         g = torch.empty(1, dtype=torch.float32, device=x.device)
         mode = GLOBAL_COMPUTE
     else:
-        _device_tensor(global_scale, "global_scale")
-        if global_scale.dtype != torch.float32 or global_scale.numel() != 1:
-            raise ValueError("global_scale must be one float32")
         g = global_scale
         mode = GLOBAL_GIVEN
     _check(library().nvfp4_quantize(_ptr(x), dt, rows, k, ldx,
@@ -166,19 +184,20 @@ def harmonize_group(scales, k, row_offsets, module_globals,
     module_globals: float32 GPU tensor [n_modules].  Returns the shared
     global (float32 GPU tensor [1]).
     """
-    _device_tensor(scales, "scales")
-    _device_tensor(module_globals, "module_globals")
+    _device_tensor(scales, "scales", torch.uint8)
     n_mod = len(row_offsets) - 1
-    if module_globals.dtype != torch.float32 or \
-            module_globals.numel() != n_mod or \
-            not module_globals.is_contiguous():
+    _device_tensor(module_globals, "module_globals", torch.float32, n_mod,
+                   scales.device)
+    if not module_globals.is_contiguous():
         raise ValueError("module_globals must be float32 [n_modules]")
-    if not scales.is_contiguous() or scales.dtype != torch.uint8 or \
+    if not scales.is_contiguous() or \
             scales.shape != (row_offsets[-1], k // 16):
         raise ValueError("scales must be contiguous uint8 [n_total, k/16]")
     if shared_global is None:
         shared_global = torch.empty(1, dtype=torch.float32,
                                     device=scales.device)
+    else:
+        _global_tensor(shared_global, "shared_global", scales.device)
     offs = (ctypes.c_int64 * (n_mod + 1))(*[int(v) for v in row_offsets])
     _check(library().nvfp4_harmonize_group(_ptr(scales), k, offs, n_mod,
                                            _ptr(module_globals),
@@ -191,13 +210,8 @@ def gemm(a, b, out_dtype=torch.bfloat16, epilogue="none", out=None):
     """Y = g_a g_b * A_hat B_hat^T for NVFP4 operands a [m, k] and b [n, k]
     (weights, K-major).  epilogue: "none", "alpha" (exp(-softplus(y))) or
     "beta" (sigmoid(y)).  Returns a [m, n] float32 or bfloat16 tensor."""
-    ac, as_, ag = a
-    bc, bs, bg = b
-    for t, nm in ((ac, "a.codes"), (as_, "a.scales"), (ag, "a.global_scale"),
-                  (bc, "b.codes"), (bs, "b.scales"), (bg, "b.global_scale")):
-        _device_tensor(t, nm)
-        if not t.is_contiguous():
-            raise ValueError("%s must be contiguous" % nm)
+    ac, as_, ag = _nvfp4_parts(a, "a")
+    bc, bs, bg = _nvfp4_parts(b, "b", ac.device)
     m, k = ac.shape[0], ac.shape[1] * 2
     n = bc.shape[0]
     if bc.shape[1] * 2 != k or as_.shape != (m, k // 16) or \
@@ -213,9 +227,10 @@ def gemm(a, b, out_dtype=torch.bfloat16, epilogue="none", out=None):
         raise ValueError("epilogue must be one of %s" % sorted(EPILOGUES))
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=ac.device)
-    elif out.dtype != out_dtype or out.dim() != 2 or out.shape != (m, n) \
-            or out.stride(1) != 1:
-        raise ValueError("out has the wrong dtype, shape or layout")
+    else:
+        _device_tensor(out, "out", out_dtype, device=ac.device)
+        if out.dim() != 2 or out.shape != (m, n) or out.stride(1) != 1:
+            raise ValueError("out has the wrong shape or layout")
     _check(library().w4a4_gemm(_ptr(ac), _ptr(as_), _ptr(ag), m, _ptr(bc),
                                _ptr(bs), _ptr(bg), n, k, _ptr(out), od,
                                out.stride(0) if m > 1 else n,
@@ -233,29 +248,29 @@ def gemm_quantize_a(x, w, global_scale=None, out_dtype=torch.bfloat16,
     (NVFP4 of x, Y [m, n] of out_dtype), both bit-identical to the two
     separate calls."""
     dt, m, k, ldx = _x_args(x)
-    wc, ws, wg = _nvfp4_parts(w, "w")
+    wc, ws, wg = _nvfp4_parts(w, "w", x.device)
     n = wc.shape[0]
     if wc.shape[1] * 2 != k or ws.shape != (n, k // 16):
         raise ValueError("operand shapes disagree")
     od = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}.get(out_dtype)
     if od is None:
         raise ValueError("out_dtype must be float32 or bfloat16")
+    if global_scale is not None:
+        _global_tensor(global_scale, "global_scale", x.device)
+    if out is not None:
+        _device_tensor(out, "out", out_dtype, device=x.device)
+        if out.dim() != 2 or out.shape != (m, n) or out.stride(1) != 1:
+            raise ValueError("out has the wrong shape or layout")
     codes = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
     scales = torch.empty((m, k // 16), dtype=torch.uint8, device=x.device)
     if global_scale is None:
         g = torch.empty(1, dtype=torch.float32, device=x.device)
         mode = GLOBAL_COMPUTE
     else:
-        _device_tensor(global_scale, "global_scale")
-        if global_scale.dtype != torch.float32 or global_scale.numel() != 1:
-            raise ValueError("global_scale must be one float32")
         g = global_scale
         mode = GLOBAL_GIVEN
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=x.device)
-    elif out.dtype != out_dtype or out.dim() != 2 or out.shape != (m, n) \
-            or out.stride(1) != 1:
-        raise ValueError("out has the wrong dtype, shape or layout")
     _check(library().w4a4_gemm_quantize_a(
         _ptr(x), dt, m, k, ldx, _ptr(codes), _ptr(scales), _ptr(g), mode,
         _ptr(wc), _ptr(ws), _ptr(wg), n, _ptr(out), od,
@@ -264,13 +279,18 @@ def gemm_quantize_a(x, w, global_scale=None, out_dtype=torch.bfloat16,
     return NVFP4(codes, scales, g), out
 
 
-def _nvfp4_parts(q, name):
+def _nvfp4_parts(q, name, device=None):
+    """Codes (uint8 [rows, k/2]), scales (uint8 [rows, k/16]) and global
+    (float32 [1]) of an NVFP4 operand, checked to be contiguous GPU tensors
+    of those types on one device (`device` when given)."""
     codes, scales, g = q
-    for t, nm in ((codes, name + ".codes"), (scales, name + ".scales"),
-                  (g, name + ".global_scale")):
-        _device_tensor(t, nm)
-        if not t.is_contiguous():
-            raise ValueError("%s must be contiguous" % nm)
+    _device_tensor(codes, name + ".codes", torch.uint8, device=device)
+    device = codes.device
+    _device_tensor(scales, name + ".scales", torch.uint8, device=device)
+    _global_tensor(g, name + ".global_scale", device)
+    for t, nm in ((codes, name + ".codes"), (scales, name + ".scales")):
+        if t.dim() != 2 or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous 2-D tensor" % nm)
     return codes, scales, g
 
 
@@ -285,8 +305,11 @@ def dequantize(q, out_dtype=torch.bfloat16, out=None):
         raise ValueError("out_dtype must be float32 or bfloat16")
     if out is None:
         out = torch.empty((rows, k), dtype=out_dtype, device=codes.device)
-    elif out.dtype != out_dtype or out.shape != (rows, k) or out.stride(1) != 1:
-        raise ValueError("out must be [rows, k] of out_dtype with unit column stride")
+    else:
+        _device_tensor(out, "out", out_dtype, device=codes.device)
+        if out.dim() != 2 or out.shape != (rows, k) or out.stride(1) != 1:
+            raise ValueError("out must be [rows, k] of out_dtype with unit "
+                             "column stride")
     ldo = out.stride(0) if rows > 1 else k
     _check(library().nvfp4_dequantize(_ptr(codes), _ptr(scales), _ptr(g), rows,
                                       k, _ptr(out), od, ldo, _stream(codes)),
@@ -308,7 +331,7 @@ def error_stats(x, q):
     dequantised value.  Relative error = sqrt(sum col 1 / sum col 0);
     max/RMS of a row = col 2 / sqrt(col 0 / k)."""
     _device_tensor(x, "x")
-    codes, scales, g = _nvfp4_parts(q, "q")
+    codes, scales, g = _nvfp4_parts(q, "q", x.device)
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit stride along k")
     dt = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}.get(x.dtype)
@@ -334,15 +357,15 @@ def gdn_gates(x, w_ba, n_beta, a_log, dt_bias, out=None):
     alpha = exp(-exp(A_log) * softplus(a + dt_bias)); a_log and dt_bias are
     float32 GPU tensors [n_alpha].  out=(beta, alpha) supplies buffers."""
     xc, xs, xg = _nvfp4_parts(x, "x")
-    wc, ws, wg = _nvfp4_parts(w_ba, "w_ba")
+    wc, ws, wg = _nvfp4_parts(w_ba, "w_ba", xc.device)
     m, k = xc.shape[0], xc.shape[1] * 2
     n = wc.shape[0]
     n_alpha = n - n_beta
     if wc.shape[1] * 2 != k or not 0 <= n_beta <= n:
         raise ValueError("x and w_ba disagree in k, or n_beta is out of range")
     for t, nm in ((a_log, "a_log"), (dt_bias, "dt_bias")):
-        _device_tensor(t, nm)
-        if t.dtype != torch.float32 or t.numel() != n_alpha or not t.is_contiguous():
+        _device_tensor(t, nm, torch.float32, n_alpha, xc.device)
+        if not t.is_contiguous():
             raise ValueError("%s must be float32 [n_alpha]" % nm)
     if out is None:
         beta = torch.empty((m, n_beta), dtype=torch.float32, device=xc.device)
@@ -350,7 +373,8 @@ def gdn_gates(x, w_ba, n_beta, a_log, dt_bias, out=None):
     else:
         beta, alpha = out
     for t, nm, cols in ((beta, "beta", n_beta), (alpha, "alpha", n_alpha)):
-        if t.dtype != torch.float32 or t.shape != (m, cols) or t.stride(1) != 1:
+        _device_tensor(t, nm, torch.float32, device=xc.device)
+        if t.dim() != 2 or t.shape != (m, cols) or t.stride(1) != 1:
             raise ValueError("%s must be float32 [m, %d] with unit column stride" % (nm, cols))
     ldb = beta.stride(0) if m > 1 else max(n_beta, 1)
     lda = alpha.stride(0) if m > 1 else max(n_alpha, 1)
@@ -363,8 +387,8 @@ def gdn_gates(x, w_ba, n_beta, a_log, dt_bias, out=None):
     return beta, alpha
 
 
-def _x_args(x, name="x"):
-    _device_tensor(x, name)
+def _x_args(x, name="x", device=None):
+    _device_tensor(x, name, device=device)
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("%s must be 2-D with unit stride along k" % name)
     dt = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}.get(x.dtype)
@@ -380,10 +404,13 @@ def fp8_kv_calibrate(tensors, amax=None):
     the device (pass amax, a float32 [1] GPU tensor, to continue an earlier
     calibration), then scale = fp32(amax / 448).  Returns (scale, amax)."""
     first = tensors[0]
+    _device_tensor(first, "calibration tensor")
+    args = [_x_args(t, "calibration tensor", first.device) for t in tensors]
     if amax is None:
         amax = torch.zeros(1, dtype=torch.float32, device=first.device)
-    for t in tensors:
-        dt, rows, k, ldx = _x_args(t, "calibration tensor")
+    else:
+        _global_tensor(amax, "amax", first.device)
+    for t, (dt, rows, k, ldx) in zip(tensors, args):
         _check(library().fp8_kv_amax_update(_ptr(t), dt, rows, k, ldx, _ptr(amax),
                                             _stream(t)), "fp8_kv_amax_update")
     scale = torch.empty(1, dtype=torch.float32, device=first.device)
@@ -396,11 +423,14 @@ def fp8_kv_cast(x, scale, out=None):
     """OCP E4M3 codes (uint8 [rows, k]) of x under the static decode scale
     (float32 [1] GPU tensor): sign | E4M3(|x| / scale), one rounding."""
     dt, rows, k, ldx = _x_args(x)
-    _device_tensor(scale, "scale")
+    _global_tensor(scale, "scale", x.device)
     if out is None:
         out = torch.empty((rows, k), dtype=torch.uint8, device=x.device)
-    elif out.dtype != torch.uint8 or out.shape != (rows, k) or out.stride(1) != 1:
-        raise ValueError("out must be uint8 [rows, k] with unit column stride")
+    else:
+        _device_tensor(out, "out", torch.uint8, device=x.device)
+        if out.dim() != 2 or out.shape != (rows, k) or out.stride(1) != 1:
+            raise ValueError("out must be uint8 [rows, k] with unit column "
+                             "stride")
     ldo = out.stride(0) if rows > 1 else k
     _check(library().fp8_kv_cast(_ptr(x), dt, rows, k, ldx, _ptr(scale), _ptr(out),
                                  ldo, _stream(x)),

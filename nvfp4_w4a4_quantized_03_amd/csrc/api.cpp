@@ -144,8 +144,9 @@ int w4a4_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
       epilogue != W4A4_EPI_BETA)
     return NVFP4_ERR_UNSUPPORTED;
   const int64_t os = out_dtype == NVFP4_DTYPE_F32 ? 4 : 2;
-  if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(out, 4) ||
-      !aligned(a_global, 4) || !aligned(b_global, 4))
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 16) ||
+      !aligned(b_scales, 16) || !aligned(out, 4) || !aligned(a_global, 4) ||
+      !aligned(b_global, 4))
     return NVFP4_ERR_MISALIGNED;
   const int64_t obytes = ((m - 1) * ldo + n) * os;
   if (overlap(out, obytes, a_codes, m * (k / 2)) ||

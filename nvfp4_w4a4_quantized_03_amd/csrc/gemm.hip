@@ -108,8 +108,8 @@ __device__ __forceinline__ float epilogue(float y) {
 // Copies one operand's BK-wide stage (ROWS rows of codes and scales) from
 // global memory to LDS through registers.
 //
-// ALIGNED (k % 128 == 0 and 16-byte aligned scale arrays, as the
-// workloads have them): every 16-byte code
+// ALIGNED (k % 128 == 0; code and scale arrays are 16-byte aligned in
+// every call): every 16-byte code
 // chunk and every row's 8 scale bytes of a stage lie inside k, so loads are
 // unconditional (rows past `rows` read a clamped, valid row) and row validity
 // is applied when storing to LDS.  No load result is consumed before the
@@ -361,17 +361,9 @@ w4a4_gemm_kernel(const uint8_t* __restrict__ a_codes,
     }
 }
 
-// LDS ring depth of the pipelined kernel (3 or 4 slots of 36 KB); 3 measured
-// ~1.5% faster than 4 (fewer loads outstanding per wave).
-#ifndef PIPE_STAGES
-#define PIPE_STAGES 3
-#endif
-// Optional scheduling hint placed after a half-stage's fragment reads (empty:
-// with LDS waits counted precisely, forcing the reads to the front of the
-// region measured ~4% slower than leaving them to the scheduler).
-#ifndef PIPE_DS_HINT
-#define PIPE_DS_HINT
-#endif
+// LDS ring depth of the pipelined kernel (slots of 36 KB); 3 measured ~1.5%
+// faster than 4 (fewer loads outstanding per wave).
+constexpr int kPipeStages = 3;
 
 // ---------------------------------------------------------------------------
 // Pipelined kernel for large, whole-stage shapes (k % 128 == 0).
@@ -643,7 +635,8 @@ __device__ __forceinline__ void pipe_stage(
       na.read(ring.a[next], ring.sa[next], arow, lane, 0);
       nb.read(ring.b[next], ring.sb[next], brow, lane, 0);
     }
-    PIPE_DS_HINT
+    // (no scheduling hint here: with LDS waits counted precisely, forcing the
+    // reads to the front of the region measured ~4% slower)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       Operands<TM, TN> nxt;
@@ -681,7 +674,7 @@ w4a4_gemm_pipelined(const uint8_t* __restrict__ a_codes,
                     int tiles_n) {
   constexpr int NW = WM * WN;
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
-  constexpr int NS = PIPE_STAGES;
+  constexpr int NS = kPipeStages;
   static_assert(NS >= 3 && NS <= 4, "ring depth");
   // one LDS object per slot (A codes, B codes, A scales, B scales)
   constexpr int kSlotBytes = (BM + BN) * (kPipeRowBytes + kPipeScaleBytes);
@@ -1256,13 +1249,10 @@ hipError_t dispatch_align(const uint8_t* a_codes, const uint8_t* a_scales,
                           const uint8_t* b_codes, const uint8_t* b_scales,
                           const float* b_global, int64_t n, int64_t k,
                           void* out, int64_t ldo, hipStream_t stream) {
-  // whole stages (k % 128 == 0) and 16-byte aligned scale arrays:
-  // unconditional 16-byte code loads and wide (8- or 16-byte) scale loads;
-  // anything else takes the guarded, byte-wise scale path
-  const bool aligned = k % kBK == 0 &&
-                       reinterpret_cast<uintptr_t>(a_scales) % 16 == 0 &&
-                       reinterpret_cast<uintptr_t>(b_scales) % 16 == 0;
-  if (aligned)
+  // whole stages (k % 128 == 0; the caller has checked 16-byte aligned
+  // code and scale arrays): unconditional 16-byte code loads and wide (8- or
+  // 16-byte) scale loads; ragged k takes the guarded, byte-wise path
+  if (k % kBK == 0)
     return dispatch_shape<true, OUT, EPI>(a_codes, a_scales, a_global, m,
                                           b_codes, b_scales, b_global, n, k,
                                           out, ldo, stream);

@@ -34,8 +34,9 @@ from .quantize import (quantize, quantize_exact, dequantize, global_scale,
 from .harmonize import harmonize, harmonize_exact
 from .fp8kv import (kv_amax, kv_scale, kv_cast, kv_decode, kv_cast_exact,
                     kv_scale_exact)
-from .gemm import (gemm_exact_int, gemm_f64, gemm_f64_rows_cols, gate_alpha,
-                   gate_beta, decoded_units, gdn_gates)
+from .gemm import (gemm_exact_int, gemm_f64, gemm_f64_rows_cols,
+                   gemm_f64_row_blocks, gate_alpha, gate_beta, decoded_units,
+                   gdn_gates)
 
 __all__ = [
     "E2M1_MAG", "e2m1_decode", "e4m3_decode", "e4m3_decode_table",
@@ -47,6 +48,7 @@ __all__ = [
     "harmonize", "harmonize_exact",
     "kv_amax", "kv_scale", "kv_cast", "kv_decode", "kv_cast_exact",
     "kv_scale_exact",
-    "gemm_exact_int", "gemm_f64", "gemm_f64_rows_cols", "gate_alpha",
+    "gemm_exact_int", "gemm_f64", "gemm_f64_rows_cols", "gemm_f64_row_blocks",
+    "gate_alpha",
     "gate_beta", "decoded_units", "gdn_gates",
 ]

@@ -67,6 +67,21 @@ def gemm_f64(a_codes, a_scales, a_global, b_codes, b_scales, b_global):
     return (a @ b.T) * float(a_global) * float(b_global)
 
 
+def gemm_f64_row_blocks(a_codes, a_scales, a_global, b_codes, b_scales,
+                        b_global, rows_per_block=2048):
+    """gemm_f64 of a tall A, one block of rows at a time: yields
+    (first_row, y_block).  B is decoded once; every block is computed
+    exactly as gemm_f64 computes those rows (it bounds host memory for the
+    full-size configurations, nothing else)."""
+    b = _decoded_f64(b_codes, b_scales).T.copy()
+    scale = float(a_global) * float(b_global)
+    rows = np.asarray(a_codes).shape[0]
+    for r0 in range(0, rows, rows_per_block):
+        a = _decoded_f64(a_codes[r0:r0 + rows_per_block],
+                         a_scales[r0:r0 + rows_per_block])
+        yield r0, (a @ b) * scale
+
+
 def gemm_f64_rows_cols(a_codes, a_scales, a_global, b_codes, b_scales,
                        b_global, rows, cols):
     """The outputs y[rows][:, cols] only (sampled check of a large GEMM)."""

@@ -114,6 +114,8 @@ def test_gemm_validation(lib):
     assert gm(lib, epi=9) == UNSUPPORTED
     assert gm(lib, a=P + 8) == MISALIGNED
     assert gm(lib, b=P + 0x300008) == MISALIGNED
+    assert gm(lib, sa=P + 0x100001) == MISALIGNED     # scale arrays 16-byte aligned
+    assert gm(lib, sb=P + 0x400008) == MISALIGNED
     assert gm(lib, out=P + 0x600002) == MISALIGNED
     assert gm(lib, out=P + 0x300010) == INVALID       # out overlaps b codes
     assert gm(lib, out=P + 0x200000 - 8) == INVALID   # out covers a_global

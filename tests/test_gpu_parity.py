@@ -376,13 +376,13 @@ def test_gemm_ragged_shapes(m, n, k):
 
 @pytest.mark.parametrize("m,n,k", [(32, 300, 512), (300, 40, 256),
                                    (200, 300, 384)])
-def test_gemm_unaligned_scale_arrays(m, n, k):
-    """Scale arrays at an odd byte offset take the guarded kernel and give
-    the same result as the oracle (the ABI puts no alignment on scales)."""
+def test_gemm_rejects_unaligned_scale_arrays(m, n, k):
+    """Scale arrays at an odd byte offset are refused with MISALIGNED on
+    the host (no kernel runs); the output buffer stays as it was."""
     rng = np.random.default_rng(m + 3 * n + k)
     xv = rng.standard_normal((m, k)).astype(np.float32)
     wv = (rng.standard_normal((n, k)) * 0.05).astype(np.float32)
-    _say("gemm unaligned scales", m, n, k)
+    _say("gemm unaligned scales refused", m, n, k)
     qa = nv.quantize(up(xv, None, "f32"))
     qb = nv.quantize(up(wv, None, "f32"))
 
@@ -392,11 +392,37 @@ def test_gemm_unaligned_scale_arrays(m, n, k):
         v.copy_(t)
         assert v.data_ptr() % 2 == 1
         return v
-    qa2 = nv.NVFP4(qa.codes, shifted(qa.scales), qa.global_scale)
-    qb2 = nv.NVFP4(qb.codes, shifted(qb.scales), qb.global_scale)
-    ref = oracle.gemm_exact_int(*oracle.quantize(xv), *oracle.quantize(wv))
-    y = host(nv.gemm(qa2, qb2, out_dtype=torch.float32)).astype(np.float64)
+    y = torch.full((m, n), 5.0, dtype=torch.float32, device=DEV)
+    for a, b in ((nv.NVFP4(qa.codes, shifted(qa.scales), qa.global_scale), qb),
+                 (qa, nv.NVFP4(qb.codes, shifted(qb.scales), qb.global_scale))):
+        with pytest.raises(nv.NVFP4Error, match="MISALIGNED"):
+            nv.gemm(a, b, out_dtype=torch.float32, out=y)
+    assert torch.all(y == 5.0)
+
+
+@pytest.mark.parametrize("m,n,k", [(5 * 256 + 17, 8 * 256, 384),    # 6 x 8 tiles
+                                   (11 * 256 + 1, 2 * 256, 256),    # 12 x 2 tiles
+                                   (5 * 256 + 17, 8 * 256, 400),    # ragged k: staged
+                                   (11 * 256 + 1, 2 * 256, 272)])
+def test_gemm_xcd_tile_order_partial_group(m, n, k):
+    """Tile counts divisible by 8 (the XCD-aware tile order) with a tile
+    row count that leaves the last group of 8 M-tiles partial, for the
+    pipelined kernel (k % 128 == 0) and the staged one (ragged k); every
+    output compared."""
+    rng = np.random.default_rng(m + n + k)
+    xv = rng.standard_normal((m, k)).astype(np.float32)
+    wv = (rng.standard_normal((n, k)) * 0.05).astype(np.float32)
+    tiles_m, tiles_n = -(-m // 256), -(-n // 256)
+    assert (tiles_m * tiles_n) % 8 == 0 and tiles_m % 8 != 0
+    _say("gemm xcd tile order", m, n, k, tiles_m, tiles_n)
+    qa = nv.quantize(up(xv, None, "f32"))
+    qb = nv.quantize(up(wv, None, "f32"))
+    ref = oracle.gemm_f64(*oracle.quantize(xv), *oracle.quantize(wv))
+    y = host(nv.gemm(qa, qb, out_dtype=torch.float32)).astype(np.float64)
     assert rel_frob(y, ref) <= TOL
+    # every element, not just the norm: a misplaced tile fails here
+    assert np.all(np.abs(y - ref) <= 1e-4 * np.max(np.abs(ref)))
+    check_bf16_within_one_ulp(nv.gemm(qa, qb, out_dtype=torch.bfloat16), ref)
 
 
 def test_gemm_strided_output():
@@ -621,6 +647,14 @@ def test_gdn_gates(m, n_beta, n_alpha, k):
         assert rel_frob(host(beta).astype(np.float64), beta_ref) <= TOL
     if n_alpha:
         assert rel_frob(host(alpha).astype(np.float64), alpha_ref) <= TOL
+    # element by element, within what fp32 accumulation and evaluation allow
+    from test_gpu_fullsize import abs_product, check_gate
+    oq = (oracle.quantize(xv), oracle.quantize(wv))
+    sabs = abs_product(*oq)
+    if n_beta:
+        check_gate(host(beta), "beta", y[:, :n_beta], sabs[:, :n_beta], k)
+    if n_alpha:
+        check_gate(host(alpha), "gdn_alpha", y[:, n_beta:], sabs[:, n_beta:], k, a_log, dt)
 
 
 def test_gdn_gates_harmonized_group_full_size():

@@ -2,8 +2,9 @@
 
 GEMM: shapes that fall on every kernel the library picks (skinny tiles for
 m or n up to 64 with either K-group size, the pipelined kernel, the staged
-kernel for ragged k or unaligned scale arrays), with ragged edges, both
-output types, the gate epilogues and strided outputs.  Bars as in
+kernel for ragged k), with ragged edges, both output types, the gate
+epilogues and strided outputs; scale arrays at an odd address are refused
+(MISALIGNED) before any launch.  Bars as in
 test_gpu_parity: fp32 output within relative Frobenius error 1e-5 of the
 exact product (gated: of the gate of it); bf16 output within one bf16 ulp
 of the exact value rounded to bf16; output columns past n untouched.
@@ -70,8 +71,8 @@ def _cases(count, seed):
 
 
 def _shifted(t):
-    """The same bytes at an odd address (scale arrays have no alignment
-    requirement in the ABI; misaligned ones take the guarded kernel)."""
+    """The same bytes at an odd address (the ABI requires 16-byte aligned
+    scale arrays and refuses others)."""
     buf = torch.empty(t.numel() + 1, dtype=torch.uint8, device=DEV)
     v = buf[1:].view(t.shape)
     v.copy_(t)
@@ -88,10 +89,11 @@ def test_gemm_random_shape(case):
     wv = (rng.standard_normal((n, k)) * 0.05).astype(np.float32)
     qa = nv.quantize(up(xv, None, "f32"))
     qb = nv.quantize(up(wv, None, "f32"))
-    if case["odd_scales"]:
-        qa = nv.NVFP4(qa.codes, _shifted(qa.scales), qa.global_scale)
-        qb = nv.NVFP4(qb.codes, _shifted(qb.scales), qb.global_scale)
     od = torch.float32 if case["out"] == "f32" else torch.bfloat16
+    if case["odd_scales"]:
+        odd = nv.NVFP4(qa.codes, _shifted(qa.scales), qa.global_scale)
+        with pytest.raises(nv.NVFP4Error, match="MISALIGNED"):
+            nv.gemm(odd, qb, out_dtype=od)
     pad = case["pad"]
     big = torch.full((m, n + pad), -3.0, dtype=od, device=DEV)
     y = big[:, :n]

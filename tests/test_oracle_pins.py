@@ -482,6 +482,23 @@ def test_gemm_int_equals_f64_blas_and_concatenation():
     assert np.array_equal(sub, yf[np.ix_([3, 9], [0, 5, 23])])
 
 
+def test_gemm_row_blocks_cover_the_exact_product():
+    """The row-block generator used for full-size checks yields every row
+    once, in order, each block within float64 accumulation error of the
+    exact integer product (and ragged last block included)."""
+    rng = np.random.default_rng(33)
+    x = rng.standard_normal((37, 512)).astype(np.float32)
+    w = (rng.standard_normal((21, 512)) * 0.05).astype(np.float32)
+    xq, wq = oracle.quantize(x), oracle.quantize(w)
+    yi = oracle.gemm_exact_int(*xq, *wq)
+    seen = []
+    for r0, yb in oracle.gemm_f64_row_blocks(*xq, *wq, rows_per_block=8):
+        seen.append((r0, yb.shape[0]))
+        assert np.max(np.abs(yb - yi[r0:r0 + yb.shape[0]])) <= \
+            1e-12 * np.max(np.abs(yi))
+    assert seen == [(0, 8), (8, 8), (16, 8), (24, 8), (32, 5)]
+
+
 def test_gates_closed_forms():
     """[P3] 前提2: alpha goes through softplus and exp, beta through a
     sigmoid.  alpha = exp(-softplus(y)) = sigmoid(-y) = 1 - beta; both are
