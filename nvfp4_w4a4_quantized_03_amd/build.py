@@ -25,8 +25,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
 DEVICE = ["-x", "hip", "--offload-arch=" + ARCH,
           "-fno-gpu-flush-denormals-to-zero",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-SOURCES = ["quantize.hip", "harmonize.hip", "gemm.hip", "dequantize.hip",
-           "fp8kv.hip", "api.cpp"]
+SOURCES = ["quantize.hip", "harmonize.hip", "gemm.hip", "gemm_stream.hip",
+           "dequantize.hip", "fp8kv.hip", "api.cpp"]
 
 
 def _compile(src):

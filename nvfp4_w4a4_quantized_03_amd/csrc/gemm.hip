@@ -32,78 +32,17 @@
 #include <atomic>
 #include <stdint.h>
 
+#include "gemm_common.h"
 #include "internal.h"
 #include "quant_device.h"
 
 namespace nvfp4 {
 namespace {
 
-constexpr int kOutF32 = 0;
-constexpr int kEpiNone = 0;
-constexpr int kEpiAlpha = 1;
-constexpr int kEpiBeta = 2;
-constexpr int kEpiGdn = 3;   // gate pair of a fused b|a projection (skinny kernel only)
-
-// Arguments of the gate-pair epilogue: columns [0, n_beta) of the product
-// give beta (stored to `out`), the others alpha with per-column A_log and
-// dt_bias (stored to out2 at column col - n_beta).
-struct EpiArgs {
-  const float* a_log;
-  const float* dt_bias;
-  int64_t n_beta;
-  float* out2;
-  int64_t ldo2;
-};
-
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float float16_t __attribute__((ext_vector_type(16)));
-
 constexpr int kBK = 128;                 // K elements per LDS stage
 constexpr int kCodeBytes = kBK / 2;      // 64 code bytes per row per stage
 constexpr int kCodeStride = kCodeBytes + 16;  // padded LDS row (bytes)
 constexpr int kScalesPerRow = kBK / 16;  // 8 block scales per row per stage
-
-// Decode 8 codes (one dword, element 2j in the low nibble of byte j) with
-// one fp16 block scale into 8 exact fp16 values.
-__device__ __forceinline__ half8_t decode8(unsigned codes, half2_t sc) {
-  const half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0);
-  const half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1);
-  const half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2);
-  const half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3);
-  const half2_t q0 = p0 * sc, q1 = p1 * sc, q2 = p2 * sc, q3 = p3 * sc;
-  half8_t r;
-  r[0] = q0[0]; r[1] = q0[1]; r[2] = q1[0]; r[3] = q1[1];
-  r[4] = q2[0]; r[5] = q2[1]; r[6] = q3[0]; r[7] = q3[1];
-  return r;
-}
-
-__device__ __forceinline__ unsigned short f32_to_bf16_rne(float f) {
-  const unsigned u = __float_as_uint(f);
-  return static_cast<unsigned short>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
-
-// e^x from the hardware base-2 exponential (v_exp_f32, about 1 ulp):
-// 2^(x log2 e); the rounding of x log2 e adds |x| 2^-24 relative error.
-constexpr float kLog2e = 1.44269504088896341f;
-constexpr float kLn2 = 0.693147180559945309f;
-__device__ __forceinline__ float exp_hw(float x) {
-  return __builtin_amdgcn_exp2f(x * kLog2e);
-}
-
-template <int EPI>
-__device__ __forceinline__ float epilogue(float y) {
-  if constexpr (EPI == kEpiAlpha) {
-    // exp(-softplus(y)) = exp(-log(1 + e^y)) = 1 / (1 + e^y); the short form
-    // keeps the epilogue small enough to unroll over the accumulator tiles
-    // (which must stay in registers).  e^y overflowing to inf gives 0.
-    return 1.0f / (1.0f + expf(y));
-  } else if constexpr (EPI == kEpiBeta) {
-    return 1.0f / (1.0f + expf(-y));
-  } else {
-    return y;
-  }
-}
 
 // Copies one operand's BK-wide stage (ROWS rows of codes and scales) from
 // global memory to LDS through registers.
@@ -483,35 +422,6 @@ __device__ __forceinline__ void interleave_hint() {
   }
 }
 
-// Buffer loads of 16 or 4 bytes per lane straight into LDS, at the
-// wave-uniform `lds` plus lane * size; the source is the resource base +
-// voff + soff.  Buffer (not FLAT-encoded global) loads are used so that the
-// compiler can keep counting LDS reads in order while these are in flight:
-// a pending FLAT load may touch LDS, which makes every later LDS-read wait a
-// full drain.
-__device__ __forceinline__ void lds_buf16(__amdgpu_buffer_rsrc_t rsrc, void* lds,
-                                          unsigned voff, unsigned soff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      rsrc, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
-#endif
-}
-
-__device__ __forceinline__ void lds_buf4(__amdgpu_buffer_rsrc_t rsrc, void* lds,
-                                         unsigned voff, unsigned soff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      rsrc, (__attribute__((address_space(3))) void*)lds, 4, voff, soff, 0, 0);
-#endif
-}
-
-// s_waitcnt immediate that waits until at most `keep` vector-memory ops are
-// outstanding, without waiting on expcnt/lgkmcnt (gfx9 encoding: vmcnt[3:0],
-// expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] at [15:14]).
-constexpr int kVmcntKeepOf(int keep) {
-  return (keep & 0xF) | 0x70 | 0xF00 | ((keep >> 4) << 14);
-}
-
 // Per-lane sources of one operand's stage loads: this wave's share of the
 // ROWS x 64 code bytes (16-byte chunks, LDS order) and ROWS x 8 scale bytes
 // (dwords).  Offsets are relative to the matrix base and exclude k0.
@@ -566,17 +476,6 @@ struct PipeLoader {
                static_cast<unsigned>(k0 / 16));
   }
 };
-
-// Workgroup barrier without the memory fence that __syncthreads() implies
-// (that fence waits for every outstanding load, including the LDS fill of a
-// later stage that is meant to stay in flight).  The wait for the stage
-// that must be resident is issued explicitly before this; the empty asm
-// statements keep the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // LDS ring of NS stages; each slot is a separate __shared__ object (holding
 // A codes, B codes, A scales, B scales) so that the compiler can prove that
@@ -1230,6 +1129,11 @@ hipError_t dispatch_shape(const uint8_t* a_codes, const uint8_t* a_scales,
 #define NVFP4_ARGS a_codes, a_scales, a_global, m, b_codes, b_scales, b_global, \
                    n, k, out, ldo, stream
   if constexpr (ALIGNED) {
+    // one operand of at most 64 rows: the streaming kernel (whole 128-K
+    // chunks, 32-bit offsets within a workgroup's rows)
+    if (gemm_stream_fits(m, n, k))
+      return launch_gemm_stream(a_codes, a_scales, a_global, m, b_codes, b_scales, b_global,
+                                n, k, out, OUT, ldo, EPI, stream);
     // k % 128 == 0 here, so the skinny kernel's groups of 2 or 4 64-K
     // chunks tile k
     if (m <= 32) return launch_skinny<1, 1, 4, 1, OUT, EPI>(NVFP4_ARGS);
@@ -1287,6 +1191,11 @@ hipError_t launch_quantize_gemm(const void* x, int x_dtype, int64_t m, int64_t k
                                 float* x_global, const uint8_t* w_codes,
                                 const uint8_t* w_scales, const float* w_global, int64_t n,
                                 void* out, int out_dtype, int64_t ldo, hipStream_t stream) {
+  // the GEMM phase runs the tiles w4a4_gemm runs for the same shape
+  if (gemm_stream_fits(m, n, k))
+    return launch_quantize_gemm_stream(x, x_dtype, m, k, ldx, mode, x_codes, x_scales, x_global,
+                                       w_codes, w_scales, w_global, n, out, out_dtype, ldo,
+                                       stream);
 #define NVFP4_QG_ARGS x, m, k, ldx, mode, x_codes, x_scales, x_global, w_codes, w_scales, \
                       w_global, n, out, ldo, stream
   if (x_dtype == kDtypeF32) {

@@ -29,6 +29,26 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                        void* out, int out_dtype, int64_t ldo, int epilogue,
                        hipStream_t stream);
 
+// Streaming GEMM for shapes with one operand of at most 64 rows, whole
+// stages of K (k % 512 == 0 for up to 32 rows, k % 256 == 0 for 33-64) and
+// k <= 2^22 (gemm_stream.hip); arguments as launch_gemm.
+bool gemm_stream_fits(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemm_stream(const uint8_t* a_codes, const uint8_t* a_scales,
+                              const float* a_global, int64_t m,
+                              const uint8_t* b_codes, const uint8_t* b_scales,
+                              const float* b_global, int64_t n, int64_t k,
+                              void* out, int out_dtype, int64_t ldo, int epilogue,
+                              hipStream_t stream);
+
+// The same fused call on the streaming GEMM's tiles, for the shapes where
+// w4a4_gemm uses them (gemm_stream_fits(m, n, k)).
+hipError_t launch_quantize_gemm_stream(const void* x, int x_dtype, int64_t m, int64_t k,
+                                       int64_t ldx, int mode, uint8_t* x_codes,
+                                       uint8_t* x_scales, float* x_global,
+                                       const uint8_t* w_codes, const uint8_t* w_scales,
+                                       const float* w_global, int64_t n, void* out,
+                                       int out_dtype, int64_t ldo, hipStream_t stream);
+
 // Small-M (m <= 64) activation quantise + W4A4 GEMM in one cooperative
 // launch (gemm.hip); k % 128 == 0 and 16-byte aligned code and scale arrays
 // are checked by the caller.
