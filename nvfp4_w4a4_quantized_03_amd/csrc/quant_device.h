@@ -121,6 +121,54 @@ __device__ __forceinline__ unsigned unpack_block(const RawBlock<0>& r, float* v)
   return mx;
 }
 
+// Raw bytes of half a block (8 elements: 16 bytes of bf16, 32 of fp32).
+template <int DTYPE>
+struct RawHalf {
+  u32x4 q[DTYPE == kDtypeF32 ? 2 : 1];
+};
+
+template <int DTYPE>
+__device__ __forceinline__ void fetch_half(const uint8_t* src, RawHalf<DTYPE>& r) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(src);
+  r.q[0] = __builtin_nontemporal_load(p);
+  if constexpr (DTYPE == kDtypeF32) r.q[1] = __builtin_nontemporal_load(p + 1);
+}
+
+// Half a block as binary32 values; returns max |x| as binary32 bits.
+template <int DTYPE>
+__device__ __forceinline__ unsigned unpack_half(const RawHalf<DTYPE>& r, float* v) {
+  if constexpr (DTYPE == kDtypeF32) {
+    const u32x4 a = r.q[0], b = r.q[1];
+    const unsigned w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    unsigned mx = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[i] = __uint_as_float(w[i]);
+      mx = max(mx, w[i] & 0x7FFFFFFFu);
+    }
+    return mx;
+  } else {
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    const u32x4 a = r.q[0];
+    const unsigned w[4] = {a.x, a.y, a.z, a.w};
+    u16x2 mx = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
+    }
+    return static_cast<unsigned>(mx[0] > mx[1] ? mx[0] : mx[1]) << 16;
+  }
+}
+
+template <int DTYPE>
+__device__ __forceinline__ unsigned load_half(const uint8_t* src, float* v) {
+  RawHalf<DTYPE> r;
+  fetch_half<DTYPE>(src, r);
+  return unpack_half<DTYPE>(r, v);
+}
+
 template <int DTYPE>
 __device__ __forceinline__ unsigned load_block(const void* base, float* v) {
   RawBlock<DTYPE> r;

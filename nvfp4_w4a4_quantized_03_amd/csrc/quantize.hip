@@ -1,10 +1,15 @@
 // NVFP4 quantisation for gfx950: tensor amax -> FP32 global, block amax ->
-// E4M3 scale, E2M1 encode + pack.  The per-block encoding (exact rounding
+// E4M3 scale, E2M1 encode + pack.  The per-element encoding (exact rounding
 // decisions) is in quant_device.h.
 //
 // Work split: one lane per 16-element block; a wave streams 64 consecutive
 // blocks (2 KiB of bf16), so loads and the 8-byte code stores coalesce.  The
-// kernel is HBM-bound; the VALU work per element is kept to a few ops.
+// kernel is HBM-bound; the VALU work per element is kept to a few ops.  (Two
+// lanes per block, 16 contiguous bytes each, with the block maximum
+// exchanged over DPP and 4 scale bytes gathered per dword store, measured
+// 20% slower: the per-block scale work and exchanges add more VALU than the
+// access pattern saves.)  The self-calibration pass reads half blocks, 16
+// contiguous bytes per lane.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -48,30 +53,35 @@ quantize_kernel(const uint8_t* __restrict__ x, int64_t nblocks, int64_t kb,
 
 __global__ void amax_init_kernel(unsigned* bits) { *bits = 0u; }
 
+// max |x| over the tensor: per trip a wave reads 64 consecutive blocks,
+// lane 2j + h half h of blocks j and j + 32 (16 contiguous bytes of bf16 or
+// 32 of fp32 each); one atomic per workgroup
 template <int DTYPE>
 __global__ void __launch_bounds__(256)
 amax_kernel(const uint8_t* __restrict__ x, int64_t nblocks, int64_t kb,
             int64_t ldx_bytes, unsigned* __restrict__ out_bits) {
-  constexpr int kElemBytes = DTYPE == kDtypeF32 ? 4 : 2;
-  const bool contiguous = ldx_bytes == kb * 16 * kElemBytes;
+  constexpr int kHalfBytes = DTYPE == kDtypeF32 ? 32 : 16;
+  const bool contiguous = ldx_bytes == kb * 2 * kHalfBytes;
+  const int lane = threadIdx.x & 63, h = lane & 1;
+  const int64_t waves = static_cast<int64_t>(gridDim.x) * (blockDim.x / 64);
+  const int64_t wave0 = static_cast<int64_t>(blockIdx.x) * (blockDim.x / 64) + (threadIdx.x >> 6);
   unsigned mx = 0;
-  for (int64_t b = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-       b < nblocks; b += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const uint8_t* src;
-    if (contiguous) {
-      src = x + b * (16 * kElemBytes);
-    } else {
-      const int64_t row = b / kb;
-      src = x + row * ldx_bytes + (b - row * kb) * (16 * kElemBytes);
+  for (int64_t w = wave0; w * 64 < nblocks; w += waves) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int64_t b = w * 64 + u * 32 + (lane >> 1);
+      const int64_t bb = b < nblocks ? b : nblocks - 1;   // past the end: the last block again
+      const uint8_t* src = contiguous ? x + bb * (2 * kHalfBytes)
+                                      : block_src<DTYPE>(x, bb, false, kb, ldx_bytes);
+      float v[8];
+      mx = max(mx, load_half<DTYPE>(src + h * kHalfBytes, v));
     }
-    float v[16];
-    mx = max(mx, load_block<DTYPE>(src, v));
   }
   // wave reduction, then one atomic per workgroup
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) mx = max(mx, static_cast<unsigned>(__shfl_xor(static_cast<int>(mx), off)));
   __shared__ unsigned part[4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wave = threadIdx.x >> 6;
   if (lane == 0) part[wave] = mx;
   __syncthreads();
   if (threadIdx.x == 0) {
