@@ -111,8 +111,9 @@ int nvfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t k,
  * GEMM) and the abstract on the paper's listing page.
  *
  *   scales        device, in/out, [n_total][k/16] E4M3 bytes of the fused
- *                 weight; module i owns rows [row_offsets[i],
- *                 row_offsets[i+1]).  The codes are not touched.
+ *                 weight, 16-byte aligned (else MISALIGNED); module i owns
+ *                 rows [row_offsets[i], row_offsets[i+1]).  The codes are
+ *                 not touched.
  *   k             k >= 16, k % 16 == 0.
  *   row_offsets   HOST array of n_modules + 1 increasing values,
  *                 row_offsets[0] == 0, row_offsets[n_modules] = n_total.

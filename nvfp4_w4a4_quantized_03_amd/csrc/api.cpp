@@ -112,7 +112,7 @@ int nvfp4_harmonize_group(uint8_t* scales, int64_t k,
   const int64_t total_rows = row_offsets[n_modules];
   if (total_rows > kMaxDim || total_rows > (int64_t(1) << 39) / (k / 16))
     return NVFP4_ERR_INVALID_VALUE;
-  if (!aligned(module_globals, 4) || !aligned(shared_global, 4))
+  if (!aligned(scales, 16) || !aligned(module_globals, 4) || !aligned(shared_global, 4))
     return NVFP4_ERR_MISALIGNED;
   const int64_t sbytes = total_rows * (k / 16);
   if (overlap(shared_global, 4, module_globals, 4 * int64_t(n_modules)) ||

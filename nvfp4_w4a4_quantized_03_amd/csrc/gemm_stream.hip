@@ -12,15 +12,14 @@
 //   * A workgroup owns SR rows of S and all (up to 64) rows of L, over the
 //     whole of K; the grid is one workgroup per SR-row slice of S.
 //   * K goes in stages of KS (512 or 256).  A stage's bytes -- the SR rows'
-//     codes and scales of S, the L rows' codes and scales -- go from global
-//     memory straight into one LDS ring slot with 16-byte buffer loads
-//     (buffer_load_dwordx4 ... lds).  Consecutive lanes load consecutive
+//     codes and scales of S, the L rows' codes and scales -- are loaded with
+//     16-byte buffer loads into a register ring two stages deep, then
+//     written to one of two LDS slots.  Consecutive lanes load consecutive
 //     16-byte pieces of a row, so every load instruction reads whole
 //     128-byte lines (the MFMA-layout loads of 32 rows x 32 bytes measured
 //     2-4x slower).  Rows past the matrix and the padding of the scale
 //     regions read past the buffer resource's range and land as zeros.
-//   * NS ring slots are in flight; one wait and one workgroup barrier per
-//     stage order them (as in the pipelined kernel).
+//   * One wait and one workgroup barrier per stage order the LDS slots.
 //   * Each wave owns KS/32/NW of a stage's 16x16x32 k-steps: it reads its
 //     code dwords and scale bytes of every S and L tile from LDS, decodes
 //     them exactly to fp16 (one conversion per two codes, one packed
@@ -152,21 +151,26 @@ struct StreamLoader {
         voff[j] = r < rows ? static_cast<unsigned>(r * kblocks + part * 16) : 0x80000000u;
         stride[j] = KS / 16;
       }
+      // a repeat is read past the range too (zeros, no memory access)
+      if (i >= L::kInst) voff[j] = 0x80000000u;
     }
   }
 
   // this wave's pieces of stage `stage` into registers (16 bytes a lane per
   // instruction, consecutive lanes consecutive bytes of a row).  Every wave
-  // issues kPerWave loads (past its count, a repeat of the stage's last
-  // piece that is never stored), so that no load depends on a runtime
-  // condition.  Stages are whole (k % KS == 0), so a valid row's offset plus
-  // the stage offset stays inside that row.
-  __device__ __forceinline__ void load(int stage, u32x4 (&v)[kPerWave]) const {
+  // issues kPerWave loads (past its count, one outside the buffer that is
+  // never stored), so that no load depends on a runtime condition.  Stages are whole (k % KS == 0), so a valid row's offset plus
+  // the stage offset stays inside that row.  A stage past the last one
+  // (stage >= nst) is loaded at kPastEnd: every offset is then beyond the
+  // range of its resource (at most 128 rows x 2^21 bytes < 2^30), so the
+  // load returns zeros without a memory access, and its value is never used.
+  static constexpr unsigned kPastEnd = 0x40000000u;
+  __device__ __forceinline__ void load(int stage, int nst, u32x4 (&v)[kPerWave]) const {
+    const int st = __builtin_amdgcn_readfirstlane(stage);
 #pragma unroll
     for (int j = 0; j < kPerWave; ++j)
       v[j] = __builtin_amdgcn_raw_buffer_load_b128(
-          rsrc[j], voff[j],
-          static_cast<unsigned>(__builtin_amdgcn_readfirstlane(stage)) * stride[j], 0);
+          rsrc[j], voff[j], st < nst ? static_cast<unsigned>(st) * stride[j] : kPastEnd, 0);
   }
 
   // ... and from registers into the LDS slot (the layout the fragment reads
@@ -322,16 +326,16 @@ __device__ __forceinline__ void stream_tile(int tile, uint8_t* lds, const Stream
 
   // Register ring of D stages: every stage of K up to D stages deep is in
   // flight from the start (a workgroup's whole share when k <= D * KS).
-  // Every load is unconditional -- past the last stage the last stage is
-  // loaded again and never used -- so that the compiler's wait before each
-  // register use counts exactly the younger loads in flight (a load under a
-  // runtime condition makes it wait for all of them).
-  // (the scheduling barriers keep the loads in stage order: the register
-  // waits count on it)
+  // Every load is unconditional -- past the last stage it reads outside
+  // its buffer (zeros, no memory access) and is never used -- so that the
+  // compiler's wait before each register use counts exactly the younger
+  // loads in flight (a load under a runtime condition makes it wait for all
+  // of them).  (the scheduling barriers keep the loads in stage order: the
+  // register waits count on it)
   u32x4 buf[D][Ldr::kPerWave];
 #pragma unroll
   for (int u = 0; u < D; ++u) {
-    ldr.load(u < nst ? u : nst - 1, buf[u]);
+    ldr.load(u, nst, buf[u]);
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -350,7 +354,7 @@ __device__ __forceinline__ void stream_tile(int tile, uint8_t* lds, const Stream
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) only
       stage_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      ldr.load(st + D < nst ? st + D : nst - 1, buf[u]);
+      ldr.load(st + D, nst, buf[u]);
       __builtin_amdgcn_sched_barrier(0);
       if (st < nst) stream_compute<SR, LR, KS, kMine>(slot, acc, chunk, dw0, r, q);
     }
@@ -406,56 +410,58 @@ w4a4_gemm_stream(StreamArgs args, const float* __restrict__ s_global,
                                                    *s_global, *l_global);
 }
 
-// Register ring depth: stages of K in flight per wave, bounded by the
-// registers a wave may give them (two waves per SIMD: 256 VGPRs each).
-template <int SR, int LR, int KS, int NW>
-constexpr int stream_depth() {
-  constexpr int regs = 4 * StreamLoader<SR, LR, KS, NW>::kPerWave;   // VGPRs per stage
-  constexpr int acc = 4 * ((SR + 15) / 16) * (LR / 16);
-  constexpr int budget = 150 - acc;
-  constexpr int d = budget / regs;
-  return d >= 10 ? 10 : (d >= 2 ? d - d % 2 : 2);
-}
-
 // A streaming-GEMM configuration as a type (for the launchers below).
 template <int SR_, int LR_, int KS_, int NW_, int D_>
 struct StreamCfg {
   static constexpr int SR = SR_, LR = LR_, KS = KS_, NW = NW_, D = D_;
 };
 
-// K per stage for an L operand of l_rows rows (512, or 256 for 33-64 rows).
+// The K granularity the streaming GEMM needs for an L operand of l_rows
+// rows: 512-K stages, or 256 for 33-64 rows (which take 512 where they can).
 inline int64_t stream_stage_k(int64_t l_rows) { return l_rows <= 32 ? 512 : 256; }
 
 // Calls f(StreamCfg<...>{}) with the configuration for s_rows x l_rows x k
 // (k % stream_stage_k(l_rows) == 0):
-//   * L rows padded to 16, 32 or 64 (K stages of 512, 512, 256);
+//   * L rows padded to 16, 32 or 64 (K stages of 512; for 64, 512 or 256,
+//     below);
 //   * S rows per workgroup: about one workgroup per CU (256) when S is
-//     tall, whole 8-row groups, 16 .. 128 rows;
-//   * ring depth: the smallest of 2, 4 and the register bound that holds
-//     every stage, else the register bound.
+//     tall, 16, 24, 32, 40, 64 or 128 rows;
+//   * a register ring of two stages.  Deeper rings measured slower on the
+//     32 x 10240 x 5120 decode shape (D = 4: 12-13 us, 10: 13-16 us, against
+//     10.4-11.4 us for D = 2, with the flushed and the warm memory-side
+//     cache alike): with every stage requested at once the memory system
+//     returns them in no useful order, and the first stage's compute waits
+//     for most of the workgroup's data.
 template <int LR, int KS, int SR, class F>
-hipError_t stream_visit_d(int64_t k, F&& f) {
-  constexpr int DMAX = stream_depth<SR, LR, KS, 8>();
-  const int64_t nst = k / KS;
-  if (nst <= 2 || DMAX == 2) return f(StreamCfg<SR, LR, KS, 8, 2>{});
-  if (nst <= 4 || DMAX == 4) return f(StreamCfg<SR, LR, KS, 8, 4>{});
-  return f(StreamCfg<SR, LR, KS, 8, DMAX>{});
+hipError_t stream_visit_d(int64_t, F&& f) {
+  return f(StreamCfg<SR, LR, KS, 8, 2>{});
 }
 
 template <int LR, int KS, class F>
 hipError_t stream_visit_rows(int64_t s_rows, int64_t k, F&& f) {
   const int64_t per = (s_rows + 255) / 256;
   if (per <= 16) return stream_visit_d<LR, KS, 16>(k, f);
+  if (per <= 24) return stream_visit_d<LR, KS, 24>(k, f);
   if (per <= 32) return stream_visit_d<LR, KS, 32>(k, f);
   if (per <= 40) return stream_visit_d<LR, KS, 40>(k, f);
-  if (per <= 64) return stream_visit_d<LR, KS, 64>(k, f);
-  return stream_visit_d<LR, KS, 128>(k, f);
+  if constexpr (LR == 64 && KS == 512) {
+    return stream_visit_d<LR, KS, 64>(k, f);   // the caller keeps per <= 64
+  } else {
+    if (per <= 64) return stream_visit_d<LR, KS, 64>(k, f);
+    return stream_visit_d<LR, KS, 128>(k, f);
+  }
 }
 
+// L of 33-64 rows takes 512-K stages where the registers allow it (S slices
+// of at most 64 rows) and k is a whole number of them: 12.0 against 14.9 us
+// at 48 x 5120 x 5120, 16.1 against 17.9 us at 64 x 10240 x 5120; with
+// 128-row slices (tall S) 256-K stages (the gate shape 32768 x 64 x 5120:
+// 32.8 us, against 35.9 us for 64-row slices at 512).
 template <class F>
 hipError_t stream_visit(int64_t s_rows, int64_t l_rows, int64_t k, F&& f) {
   if (l_rows <= 16) return stream_visit_rows<16, 512>(s_rows, k, f);
   if (l_rows <= 32) return stream_visit_rows<32, 512>(s_rows, k, f);
+  if (k % 512 == 0 && (s_rows + 255) / 256 <= 64) return stream_visit_rows<64, 512>(s_rows, k, f);
   return stream_visit_rows<64, 256>(s_rows, k, f);
 }
 

@@ -57,8 +57,9 @@ __device__ __forceinline__ unsigned refold(unsigned s, float gi, float gstar, fl
   return e4m3_settle(e4m3_candidate(num / den), num, den);
 }
 
-// BPL consecutive scale bytes per lane (one load and store of BPL bytes when
-// the array is aligned to them); a lane's bytes may span module
+// BPL consecutive scale bytes per lane, one load and store of BPL bytes
+// (the array is 16-byte aligned; only the lane holding the array's last,
+// partial word goes byte by byte); a lane's bytes may span module
 // boundaries, so the module is advanced per byte.
 template <int BPL>
 __global__ void __launch_bounds__(256)
@@ -78,7 +79,7 @@ harmonize_kernel(uint8_t* __restrict__ scales, int64_t total, Offsets offs, int 
   float gi = module_globals[mod];
   int64_t next = mod + 1 < n_modules ? offs.first[mod + 1] : total;
   constexpr int kWords = BPL / 4;
-  const bool vec = (reinterpret_cast<uintptr_t>(scales) & (BPL - 1)) == 0 && i0 + BPL <= total;
+  const bool vec = i0 + BPL <= total;
   unsigned w[kWords];
 #pragma unroll
   for (int q = 0; q < kWords; ++q) w[q] = 0u;

@@ -90,6 +90,8 @@ def test_harmonize_validation(lib):
     assert h(lib, shared=P + 0x100000) == INVALID     # aliases the globals
     assert h(lib, shared=P + 4) == INVALID            # inside the scales
     assert h(lib, glob=P + 0x100002) == MISALIGNED
+    assert h(lib, scales=P + 1) == MISALIGNED         # scales not 16-byte aligned
+    assert h(lib, scales=P + 8) == MISALIGNED
     assert lib.nvfp4_harmonize_group(P, 64, None, 1, P + 0x100000,
                                      P + 0x200000, None) == INVALID
 

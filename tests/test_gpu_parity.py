@@ -254,12 +254,11 @@ def test_harmonize_every_scale_byte():
 
 
 @pytest.mark.parametrize("scale", [1.0, 2.0 ** 110, 2.0 ** -110])
-@pytest.mark.parametrize("aligned", [True, False])
-def test_harmonize_ragged_modules(scale, aligned):
+def test_harmonize_ragged_modules(scale):
     """Rows of 5 scale bytes (k = 80) and modules of 1-3 rows, so a lane's
-    bytes straddle module boundaries; a module with global 0 and two with
-    the shared maximum; the array at an odd address (byte-wise path) or
-    aligned; shared globals beyond 2^100 or below 2^-100 (float64 path)."""
+    bytes straddle module boundaries and the array ends in a partial word; a
+    module with global 0 and two with the shared maximum; shared globals
+    beyond 2^100 or below 2^-100 (float64 path)."""
     rng = np.random.default_rng(41)
     rows_per = [1, 3, 1, 2, 1, 4, 2]
     offs = [0] + list(np.cumsum(rows_per))
@@ -267,13 +266,27 @@ def test_harmonize_ragged_modules(scale, aligned):
     sc = rng.integers(0, 0x7F, (offs[-1], k // 16)).astype(np.uint8)
     gs = [np.float32(v * scale) for v in (0.3, 1.7, 0.0, 1.7, 1e-3, 0.999, 1.25)]
     ref, gstar = oracle.harmonize(sc, offs, gs)
-    buf = torch.empty(sc.size + 1, dtype=torch.uint8, device=DEV)
-    d = (buf[:sc.size] if aligned else buf[1:]).view(sc.shape)
+    buf = torch.full((sc.size + 16,), 0xA5, dtype=torch.uint8, device=DEV)
+    d = buf[:sc.size].view(sc.shape)
     d.copy_(torch.from_numpy(sc))
-    _say("harmonize ragged", scale, aligned)
+    _say("harmonize ragged", scale)
     out = nv.harmonize_group(d, k, offs, torch.tensor(gs, dtype=torch.float32, device=DEV))
     assert host(out)[0] == gstar
     assert np.array_equal(host(d), ref)
+    assert np.all(host(buf[sc.size:]) == 0xA5)   # nothing past the array
+
+
+def test_harmonize_rejects_unaligned_scales():
+    """A scale array that is not 16-byte aligned is refused before any
+    device work (no byte-wise path), and left untouched."""
+    sc = np.arange(12 * 5, dtype=np.uint8).reshape(12, 5)
+    buf = torch.zeros(sc.size + 16, dtype=torch.uint8, device=DEV)
+    d = buf[8:8 + sc.size].view(sc.shape)
+    d.copy_(torch.from_numpy(sc))
+    gs = torch.tensor([0.5, 1.0], dtype=torch.float32, device=DEV)
+    with pytest.raises(nv.NVFP4Error, match="MISALIGNED"):
+        nv.harmonize_group(d, 80, [0, 8, 12], gs)
+    assert np.array_equal(host(d), sc)
 
 
 def test_harmonize_most_modules():
@@ -398,6 +411,46 @@ def test_gemm_rejects_unaligned_scale_arrays(m, n, k):
         with pytest.raises(nv.NVFP4Error, match="MISALIGNED"):
             nv.gemm(a, b, out_dtype=torch.float32, out=y)
     assert torch.all(y == 5.0)
+
+
+# (m, n, k): one operand of at most 64 rows (L) and k a whole number of
+# 512-K stages (L <= 32 rows) or 256-K stages (33..64 rows), so w4a4_gemm
+# streams the other operand (S); S sized so that every S-rows-per-workgroup
+# choice (16, 24, 32, 40, 64, 128: about one workgroup per CU) and every L
+# padding (16, 32, 64) is taken, S = B (decode) and S = A (gate
+# projections), each with a ragged last workgroup.
+STREAM_SHAPES = [(7, 4109, 512),      # S rows per workgroup 24, L 16
+                 (32, 5120, 1024),    # 24, L 32
+                 (48, 6001, 512),     # 24, L 64, 512-K stages
+                 (64, 2100, 256),     # 16, L 64, 256-K stages
+                 (20, 8000, 512),     # 32, L 32
+                 (3, 10007, 512),     # 40, L 16
+                 (33, 12000, 256),    # 64, L 64, 256-K stages
+                 (16, 20003, 512),    # 128, L 16
+                 (6001, 48, 256),     # S = A: 24, L 64, 256-K stages
+                 (12000, 40, 512),    # S = A: 64, L 64, 512-K stages
+                 (20000, 64, 512),    # S = A: 128, L 64, 256-K stages
+                 (20000, 32, 512),    # S = A: 128, L 32
+                 (4100, 8, 1024)]     # S = A: 24, L 16
+
+
+@pytest.mark.parametrize("m,n,k", STREAM_SHAPES)
+def test_gemm_streaming_configurations(m, n, k):
+    """Every output of the streaming GEMM's configurations against the
+    exact product, fp32 and bf16, and the beta gate."""
+    rng = np.random.default_rng(7 * m + 5 * n + k)
+    xv = rng.standard_normal((m, k)).astype(np.float32)
+    wv = (rng.standard_normal((n, k)) * 0.05).astype(np.float32)
+    _say("gemm streaming", m, n, k)
+    qa = nv.quantize(up(xv, None, "f32"))
+    qb = nv.quantize(up(wv, None, "f32"))
+    ref = oracle.gemm_f64(*oracle.quantize(xv), *oracle.quantize(wv))
+    y = host(nv.gemm(qa, qb, out_dtype=torch.float32)).astype(np.float64)
+    assert rel_frob(y, ref) <= TOL
+    assert np.all(np.abs(y - ref) <= 1e-4 * np.max(np.abs(ref)))
+    check_bf16_within_one_ulp(nv.gemm(qa, qb, out_dtype=torch.bfloat16), ref)
+    yb = host(nv.gemm(qa, qb, out_dtype=torch.float32, epilogue="beta"))
+    assert rel_frob(yb.astype(np.float64), oracle.gate_beta(ref)) <= TOL
 
 
 @pytest.mark.parametrize("m,n,k", [(5 * 256 + 17, 8 * 256, 384),    # 6 x 8 tiles
