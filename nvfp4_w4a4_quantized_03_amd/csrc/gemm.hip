@@ -913,16 +913,10 @@ skinny_tile(int tile, const uint8_t* __restrict__ a_codes,
           const float y = static_cast<float>(static_cast<double>(sum) * gab);
           if constexpr (EPI == kEpiGdn) {
             if (col < ep.n_beta) {
-              static_cast<float*>(out)[row * ldo + col] =
-                  __builtin_amdgcn_rcpf(1.0f + exp_hw(-y));
+              static_cast<float*>(out)[row * ldo + col] = gdn_beta(y);
             } else {
-              // alpha = exp(-exp(A_log) softplus(a + dt_bias)),
-              // softplus(x) = max(x, 0) + log(1 + e^-|x|)
               const int64_t j = col - ep.n_beta;
-              const float x = y + ep.dt_bias[j];
-              const float sp = fmaxf(x, 0.0f) +
-                               __builtin_amdgcn_logf(1.0f + exp_hw(-fabsf(x))) * kLn2;
-              ep.out2[row * ep.ldo2 + j] = exp_hw(-exp_hw(ep.a_log[j]) * sp);
+              ep.out2[row * ep.ldo2 + j] = gdn_alpha(y, ep.a_log[j], ep.dt_bias[j]);
             }
           } else if constexpr (OUT == kOutF32) {
             static_cast<float*>(out)[row * ldo + col] = epilogue<EPI>(y);
@@ -1215,6 +1209,10 @@ hipError_t launch_gdn_gates(const uint8_t* x_codes, const uint8_t* x_scales,
                             float* beta_out, int64_t ld_beta, float* alpha_out,
                             int64_t ld_alpha, hipStream_t stream) {
   const int64_t n = n_beta + n_alpha;
+  if (gdn_stream_fits(m, n, k))
+    return launch_gdn_stream(x_codes, x_scales, x_global, m, w_codes, w_scales, w_global, n_beta,
+                             n_alpha, k, a_log, dt_bias, beta_out, ld_beta, alpha_out, ld_alpha,
+                             stream);
   const EpiArgs ep{a_log, dt_bias, n_beta, alpha_out, ld_alpha};
 #define NVFP4_GDN_ARGS x_codes, x_scales, x_global, m, w_codes, w_scales, w_global, n, k, \
                        beta_out, ld_beta, stream, ep

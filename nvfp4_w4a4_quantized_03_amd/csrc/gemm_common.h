@@ -20,7 +20,7 @@ constexpr int kOutF32 = 0;
 constexpr int kEpiNone = 0;
 constexpr int kEpiAlpha = 1;
 constexpr int kEpiBeta = 2;
-constexpr int kEpiGdn = 3;   // gate pair of a fused b|a projection (skinny kernel only)
+constexpr int kEpiGdn = 3;   // gate pair of a fused b|a projection (w4a4_gemm_gdn_gates)
 
 // Arguments of the gate-pair epilogue: columns [0, n_beta) of the product
 // give beta (stored to `out`), the others alpha with per-column A_log and
@@ -63,6 +63,18 @@ constexpr float kLog2e = 1.44269504088896341f;
 constexpr float kLn2 = 0.693147180559945309f;
 __device__ __forceinline__ float exp_hw(float x) {
   return __builtin_amdgcn_exp2f(x * kLog2e);
+}
+
+// The gate pair of a fused b|a projection (the explainer page, section
+// 前提2): beta = sigmoid(b) and alpha = exp(-exp(A_log) softplus(a + dt_bias))
+// per head, softplus(x) = max(x, 0) + log(1 + e^-|x|).
+__device__ __forceinline__ float gdn_beta(float y) {
+  return __builtin_amdgcn_rcpf(1.0f + exp_hw(-y));
+}
+__device__ __forceinline__ float gdn_alpha(float y, float a_log, float dt_bias) {
+  const float x = y + dt_bias;
+  const float sp = fmaxf(x, 0.0f) + __builtin_amdgcn_logf(1.0f + exp_hw(-fabsf(x))) * kLn2;
+  return exp_hw(-exp_hw(a_log) * sp);
 }
 
 template <int EPI>

@@ -257,6 +257,7 @@ struct StreamArgs {
   int64_t k;
   void* out;
   int64_t ldo;
+  EpiArgs ep;   // the gate pair's (EPI == kEpiGdn only)
 };
 
 // LDS bytes of a workgroup: two stage slots, or the round of partial tiles
@@ -389,12 +390,26 @@ __device__ __forceinline__ void stream_tile(int tile, uint8_t* lds, const Stream
         const int sl = ts * 16 + c4 + i;
         const int64_t srow = s0 + sl;
         if (sl < SR && srow < s_rows && lrow < l_rows) {
-          const float y = epilogue<EPI>(static_cast<float>(static_cast<double>(sum[i]) * gab));
-          const int64_t o = S_IS_M ? srow * ldo + lrow : lrow * ldo + srow;
-          if constexpr (OUT == kOutF32)
-            static_cast<float*>(out)[o] = y;
-          else
-            static_cast<unsigned short*>(out)[o] = f32_to_bf16_rne(y);
+          const float yg = static_cast<float>(static_cast<double>(sum[i]) * gab);
+          if constexpr (EPI == kEpiGdn) {
+            // S = the activations, L = the fused b|a weight: column lrow is
+            // beta below n_beta, alpha of head lrow - n_beta above
+            static_assert(S_IS_M && OUT == kOutF32, "gate pair: Y[token][head], fp32");
+            const EpiArgs& ep = args.ep;
+            if (lrow < ep.n_beta) {
+              static_cast<float*>(out)[srow * ldo + lrow] = gdn_beta(yg);
+            } else {
+              const int64_t j = lrow - ep.n_beta;
+              ep.out2[srow * ep.ldo2 + j] = gdn_alpha(yg, ep.a_log[j], ep.dt_bias[j]);
+            }
+          } else {
+            const float y = epilogue<EPI>(yg);
+            const int64_t o = S_IS_M ? srow * ldo + lrow : lrow * ldo + srow;
+            if constexpr (OUT == kOutF32)
+              static_cast<float*>(out)[o] = y;
+            else
+              static_cast<unsigned short*>(out)[o] = f32_to_bf16_rne(y);
+          }
         }
       }
     }
@@ -601,6 +616,26 @@ hipError_t launch_quantize_gemm_stream_t(const void* x, int64_t ldx, int mode, f
 }
 
 }  // namespace
+
+// The gate pair takes the streaming GEMM for up to 64 gate columns (L = the
+// fused b|a weight); wider pairs stay on the skinny kernel: with 128 L rows,
+// 64-row S slices need two rounds of workgroups (32768 x 128 x 5120: 76.5 us
+// against 70-72 us), and 128-row slices on 4 waves spill.
+bool gdn_stream_fits(int64_t m, int64_t n, int64_t k) {
+  return m >= 1 && n >= 1 && n <= 64 && k <= (int64_t{1} << 22) && k % stream_stage_k(n) == 0;
+}
+
+hipError_t launch_gdn_stream(const uint8_t* x_codes, const uint8_t* x_scales,
+                             const float* x_global, int64_t m, const uint8_t* w_codes,
+                             const uint8_t* w_scales, const float* w_global, int64_t n_beta,
+                             int64_t n_alpha, int64_t k, const float* a_log,
+                             const float* dt_bias, float* beta_out, int64_t ld_beta,
+                             float* alpha_out, int64_t ld_alpha, hipStream_t stream) {
+  const int64_t n = n_beta + n_alpha;
+  const StreamArgs args{x_codes, x_scales, m, w_codes, w_scales, n, k, beta_out, ld_beta,
+                        EpiArgs{a_log, dt_bias, n_beta, alpha_out, ld_alpha}};
+  return launch_stream<true, kOutF32, kEpiGdn>(args, x_global, w_global, stream);
+}
 
 bool gemm_stream_fits(int64_t m, int64_t n, int64_t k) {
   if (!(m <= 64 || n <= 64) || k > (int64_t{1} << 22)) return false;

@@ -59,6 +59,17 @@ hipError_t launch_quantize_gemm(const void* x, int x_dtype, int64_t m, int64_t k
                                 const uint8_t* w_scales, const float* w_global, int64_t n,
                                 void* out, int out_dtype, int64_t ldo, hipStream_t stream);
 
+// The gate pair on the streaming GEMM (gemm_stream.hip): S = the
+// activations, L = the fused b|a weight of n <= 64 rows, k a whole number
+// of its stages (k % 512 for n <= 32, k % 256 otherwise) and k <= 2^22.
+bool gdn_stream_fits(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gdn_stream(const uint8_t* x_codes, const uint8_t* x_scales,
+                             const float* x_global, int64_t m, const uint8_t* w_codes,
+                             const uint8_t* w_scales, const float* w_global, int64_t n_beta,
+                             int64_t n_alpha, int64_t k, const float* a_log,
+                             const float* dt_bias, float* beta_out, int64_t ld_beta,
+                             float* alpha_out, int64_t ld_alpha, hipStream_t stream);
+
 // Gate pair of a fused b|a projection (gemm.hip); k % 128 == 0, 16-byte
 // aligned scale arrays and n_beta + n_alpha <= 256 are checked by the caller.
 constexpr int64_t kMaxGateCols = 256;

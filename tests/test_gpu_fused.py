@@ -71,10 +71,16 @@ def _check_against_separate_and_oracle(xv, xd, wv, qw, gt, out_dtype):
         check_bf16_within_one_ulp(y, ref)
 
 
+# k a whole number of streaming stages takes the streaming GEMM's tiles
+# (incl. 24-row S slices: (7, 4109, 512), (64, 4100, 1024); 40-row slices:
+# (20, 10007, 512); 33-64-row L with 512-K stages: (48, 6001, 512)), other k
+# the skinny kernel's
 @pytest.mark.parametrize("m,n,k", [(1, 1, 128), (1, 64, 128), (7, 100, 384),
                                    (32, 300, 512), (33, 96, 256),
                                    (64, 130, 640), (17, 33, 1024),
-                                   (64, 4100, 1024), (2, 1000, 5120)])
+                                   (64, 4100, 1024), (2, 1000, 5120),
+                                   (7, 4109, 512), (48, 6001, 512),
+                                   (20, 10007, 512)])
 @pytest.mark.parametrize("xdt,mode", [("f32", "compute"), ("bf16", "compute"),
                                       ("f32", "given"), ("bf16", "given")])
 def test_fused_matches_separate_calls(m, n, k, xdt, mode):

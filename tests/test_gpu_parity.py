@@ -681,10 +681,16 @@ def _gate_params(n_alpha, seed):
     return a_log, dt, torch.from_numpy(a_log).to(DEV), torch.from_numpy(dt).to(DEV)
 
 
+# k % 256 == 0 (% 512 for n <= 32) with n = n_beta + n_alpha <= 64 takes the
+# streaming GEMM (S = the tokens; L of 16, 32 or 64 rows), other shapes the
+# skinny kernel
 @pytest.mark.parametrize("m,n_beta,n_alpha,k", [(1, 16, 16, 128), (37, 64, 64, 5120),
                                                 (300, 32, 48, 384), (513, 100, 120, 256),
                                                 (64, 0, 20, 128), (40, 24, 0, 256),
-                                                (70, 128, 128, 640)])
+                                                (70, 128, 128, 640),
+                                                (1000, 64, 64, 512), (20000, 64, 64, 256),
+                                                (33, 0, 40, 512), (5000, 20, 12, 1024),
+                                                (3000, 60, 4, 256), (4100, 7, 9, 512)])
 def test_gdn_gates(m, n_beta, n_alpha, k):
     rng = np.random.default_rng(m + n_beta + 3 * n_alpha + k)
     xv = rng.standard_normal((m, k)).astype(np.float32)
