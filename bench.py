@@ -33,7 +33,7 @@ PEAK_MFMA_TFLOPS = 2500.0        # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBPS = 8000.0           # MI355X HBM3E
 M, M_DEC, N, K = 32768, 32, 10240, 5120
 WORKLOAD = 5
-KERNEL_SOURCES = ["gemm.hip", "quantize.hip", "quant_device.h"]
+KERNEL_SOURCES = ["gemm.hip", "gemm_stream.hip", "quantize.hip", "quant_device.h"]
 
 
 def parse():
@@ -136,20 +136,46 @@ def cpu_baseline():
     }
 
 
-def _time(fn, reps, stream):
-    """Average GPU time (us) of fn() over reps launches (HIP events on the
-    launch stream), after one warm-up call."""
+MALL_BYTES = 256 * 2 ** 20   # MI355X memory-side (infinity) cache
+
+
+def _time(fn, reps, stream, runs=20):
+    """Median GPU time (us) of one call of fn() (HIP events on the launch
+    stream): one warm-up call, then `runs` timed batches of calls, a batch
+    long enough (>= ~200 us) that the event pair's own cost is small.  fn may
+    be a list of equivalent calls on different buffers, used in turn (to
+    keep inputs that fit the memory-side cache from being timed warm).
+    `reps` is kept for callers and ignored (the batch size is chosen here)."""
     import torch
-    fn()
+    fns = fn if isinstance(fn, (list, tuple)) else [fn]
+    fns[0]()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for _ in range(reps):
-        fn()
+    fns[1 % len(fns)]()
     e1.record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / reps
+    one = max(e0.elapsed_time(e1) * 1e3, 1.0)
+    batch = int(min(64, max(1, np.ceil(200.0 / one))))
+    times, i = [], 0
+    for _ in range(runs):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(batch):
+            fns[i % len(fns)]()
+            i += 1
+        b.record(stream)
+        times.append((a, b))
+    torch.cuda.synchronize()
+    return float(np.median([x.elapsed_time(y) * 1e3 / batch for x, y in times]))
+
+
+def _copies(nbytes):
+    """How many copies of an nbytes input to rotate through so that they
+    exceed twice the memory-side cache."""
+    return int(max(1, np.ceil(2 * MALL_BYTES / nbytes)))
 
 
 def other_workloads(nv, synth, dev, stream, reps=10):
@@ -161,7 +187,9 @@ def other_workloads(nv, synth, dev, stream, reps=10):
     dequantisation to bf16 plus per-row error statistics of the 32768x5120
     activations, the decode projection's activation quantisation + GEMM as
     two calls and as one fused launch, and the FP8 KV-cache scale
-    calibration and cast of a 32768x1024 bf16 slab."""
+    calibration and cast of a 32768x1024 bf16 slab.  Each figure is the
+    median of 20 timed batches of calls; bandwidth-bound calls whose inputs
+    fit the memory-side cache rotate over copies of them."""
     import numpy as np
     import torch
 
@@ -172,12 +200,23 @@ def other_workloads(nv, synth, dev, stream, reps=10):
         return torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16)
 
     out = {}
-    # in_proj: X[4096x5120], W[12288x5120]
+    # in_proj: X[4096x5120], W[12288x5120]; both quantisations rotate over
+    # copies of their input and output (together over twice the memory-side
+    # cache), so that no call finds them cached
     x, w = up(2, "x"), up(2, "w")
     qx, qw = nv.quantize(x), nv.quantize(w)
     gx = qx.global_scale.clone()
-    t_q = _time(lambda: nv.quantize(x, global_scale=gx, out=(qx.codes, qx.scales)), reps, stream)
-    t_qw = _time(lambda: nv.quantize(w, out=(qw.codes, qw.scales)), reps, stream)
+    nxc = _copies(4096 * 5120 * 2.5625)
+    xs = [x.clone() for _ in range(nxc)]
+    qxs = [(torch.empty_like(qx.codes), torch.empty_like(qx.scales)) for _ in range(nxc)]
+    t_q = _time([lambda i=i: nv.quantize(xs[i], global_scale=gx, out=qxs[i]) for i in range(nxc)],
+                reps, stream)
+    del xs, qxs
+    nwc = _copies(12288 * 5120 * 4.5625)
+    ws = [w.clone() for _ in range(nwc)]
+    qws = [(torch.empty_like(qw.codes), torch.empty_like(qw.scales)) for _ in range(nwc)]
+    t_qw = _time([lambda i=i: nv.quantize(ws[i], out=qws[i]) for i in range(nwc)], reps, stream)
+    del ws, qws
     y = torch.empty((4096, 12288), dtype=torch.bfloat16, device=dev)
     t_g = _time(lambda: nv.gemm(qx, qw, out_dtype=torch.bfloat16, out=y), reps, stream)
     fl = 2.0 * 4096 * 12288 * 5120
@@ -186,14 +225,19 @@ def other_workloads(nv, synth, dev, stream, reps=10):
         "quantize_w_compute_us": t_qw,
         "gemm_us": t_g, "gemm_tflops": fl / t_g / 1e6}
     del x, w, qx, qw, y
-    # gate projections: X[32768x5120], W_a/W_b[64x5120], fp32 out + gates
+    # gate projections: X[32768x5120], W_a/W_b[64x5120], fp32 out + gates;
+    # the 94 MB of quantised activations fit the memory-side cache, so the
+    # calls rotate over copies of them
     x = up(3, "x")
     qx = nv.quantize(x)
+    nqc = _copies(32768 * 5120 * 0.5625)
+    qxs = [nv.NVFP4(qx.codes.clone(), qx.scales.clone(), qx.global_scale) for _ in range(nqc)]
     res = {}
     for name, epi in (("w_a", "alpha"), ("w_b", "beta")):
         qw = nv.quantize(up(3, name))
         y = torch.empty((32768, 64), dtype=torch.float32, device=dev)
-        t = _time(lambda: nv.gemm(qx, qw, out_dtype=torch.float32, epilogue=epi, out=y), reps, stream)
+        t = _time([lambda q=q: nv.gemm(q, qw, out_dtype=torch.float32, epilogue=epi, out=y)
+                   for q in qxs], reps, stream)
         byts = 32768 * 5120 * 0.5625 + 64 * 5120 * 0.5625 + 32768 * 64 * 4
         res[name + "_" + epi] = {"gemm_us": t, "gbps": byts / t / 1e3,
                                  "frac_hbm_peak": byts / t / 1e3 / PEAK_HBM_GBPS}
@@ -210,12 +254,13 @@ def other_workloads(nv, synth, dev, stream, reps=10):
     dt_bias = torch.linspace(-3.0, 3.0, 64, device=dev)
     gb = (torch.empty((32768, 64), dtype=torch.float32, device=dev),
           torch.empty((32768, 64), dtype=torch.float32, device=dev))
-    t = _time(lambda: nv.gdn_gates(qx, wba, 64, a_log, dt_bias, out=gb), reps, stream)
+    t = _time([lambda q=q: nv.gdn_gates(q, wba, 64, a_log, dt_bias, out=gb) for q in qxs],
+              reps, stream)
     byts = 32768 * 5120 * 0.5625 + 128 * 5120 * 0.5625 + 32768 * 128 * 4
     out["gdn_gates_fused_ba_32768x128x5120"] = {
         "gemm_us": t, "gbps": byts / t / 1e3,
         "frac_hbm_peak": byts / t / 1e3 / PEAK_HBM_GBPS}
-    del x, qx
+    del x, qx, qxs
     # harmonised fused group 12288|5120|128 with X[8192x5120]
     sizes = [12288, 5120, 128]
     offs = [0, 12288, 17408, 17536]
@@ -313,9 +358,15 @@ def other_workloads(nv, synth, dev, stream, reps=10):
     # FP8 KV cache: calibrate a static scale, cast a 32768 x 1024 bf16 slab
     kvx = torch.randn((32768, 1024), device=dev).to(torch.bfloat16)
     scale, amax = nv.fp8_kv_calibrate([kvx])
-    kvo = torch.empty((32768, 1024), dtype=torch.uint8, device=dev)
-    t_a = _time(lambda: nv.fp8_kv_calibrate([kvx], amax=amax), reps, stream)
-    t_k = _time(lambda: nv.fp8_kv_cast(kvx, scale, out=kvo), reps, stream)
+    # 67 MB of input: rotated over copies, as above
+    nkc = _copies(32768 * 1024 * 3)
+    kvs = [kvx.clone() for _ in range(nkc)]
+    kvos = [torch.empty((32768, 1024), dtype=torch.uint8, device=dev) for _ in range(nkc)]
+    t_a = _time([lambda i=i: nv.fp8_kv_calibrate([kvs[i]], amax=amax) for i in range(nkc)],
+                reps, stream)
+    t_k = _time([lambda i=i: nv.fp8_kv_cast(kvs[i], scale, out=kvos[i]) for i in range(nkc)],
+                reps, stream)
+    del kvs, kvos
     kv_el = 32768 * 1024
     out["fp8_kv_32768x1024_bf16"] = {
         "calibrate_us": t_a, "calibrate_gbps_2B_per_elem": kv_el * 2 / t_a / 1e3,
@@ -409,7 +460,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    # mean (the roofline's average launch duration) and median per kernel
     avg_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]]))
+              for n in names}
+    med_ms = {n: float(np.median([a.elapsed_time(b) for a, b in ev[n]]))
               for n in names}
     flops_gemm = 2.0 * M * N * K
     flops_step = 2.0 * (M + M_DEC) * N * K
@@ -459,14 +513,18 @@ def main():
                      "traffic": traffic},
         "kernels": {
             "gemm_prefill": {"us": avg_ms["gemm"] * 1e3,
+                             "us_median": med_ms["gemm"] * 1e3,
                              "tflops": gemm_tflops,
                              "frac_mfma_peak": gemm_tflops / PEAK_MFMA_TFLOPS},
             "quantize_prefill": {"us": avg_ms["quantize"] * 1e3,
+                                 "us_median": med_ms["quantize"] * 1e3,
                                  "gbps": q_gbps,
                                  "frac_hbm_peak": q_gbps / PEAK_HBM_GBPS,
                                  "bytes": q_bytes},
-            "quantize_decode": {"us": avg_ms["quantize_dec"] * 1e3},
+            "quantize_decode": {"us": avg_ms["quantize_dec"] * 1e3,
+                                "us_median": med_ms["quantize_dec"] * 1e3},
             "gemm_decode": {"us": avg_ms["gemm_dec"] * 1e3,
+                            "us_median": med_ms["gemm_dec"] * 1e3,
                             "gbps": dec_bytes / (avg_ms["gemm_dec"] * 1e-3)
                             / 1e9,
                             "frac_hbm_peak": dec_bytes /
