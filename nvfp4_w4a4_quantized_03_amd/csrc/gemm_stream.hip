@@ -126,7 +126,7 @@ struct StreamLoader {
     for (int j = 0; j < kPerWave; ++j) {
       const int i = wave + j * NW;   // instruction index in the stage
       if (i < L::kInst) ++count;
-      const int ii = i < L::kInst ? i : L::kInst - 1;   // repeat, never stored
+      const int ii = i < L::kInst ? i : L::kInst - 1;   // (past the count: never stored)
       lds[j] = static_cast<unsigned>(ii) * 1024u;
       if (ii < L::kInstSC || (ii >= L::kInstSC + L::kInstSS &&
                               ii < L::kInstSC + L::kInstSS + L::kInstLC)) {
@@ -151,7 +151,8 @@ struct StreamLoader {
         voff[j] = r < rows ? static_cast<unsigned>(r * kblocks + part * 16) : 0x80000000u;
         stride[j] = KS / 16;
       }
-      // a repeat is read past the range too (zeros, no memory access)
+      // a slot past this wave's count reads outside the range (zeros, no
+      // memory access)
       if (i >= L::kInst) voff[j] = 0x80000000u;
     }
   }
@@ -159,11 +160,12 @@ struct StreamLoader {
   // this wave's pieces of stage `stage` into registers (16 bytes a lane per
   // instruction, consecutive lanes consecutive bytes of a row).  Every wave
   // issues kPerWave loads (past its count, one outside the buffer that is
-  // never stored), so that no load depends on a runtime condition.  Stages are whole (k % KS == 0), so a valid row's offset plus
-  // the stage offset stays inside that row.  A stage past the last one
-  // (stage >= nst) is loaded at kPastEnd: every offset is then beyond the
-  // range of its resource (at most 128 rows x 2^21 bytes < 2^30), so the
-  // load returns zeros without a memory access, and its value is never used.
+  // never stored), so that no load depends on a runtime condition.  Stages
+  // are whole (k % KS == 0), so a valid row's offset plus the stage offset
+  // stays inside that row.  A stage past the last one (stage >= nst) is
+  // loaded at kPastEnd: every offset is then beyond the range of its
+  // resource (at most 128 rows x 2^21 bytes < 2^30), so the load returns
+  // zeros without a memory access, and its value is never used.
   static constexpr unsigned kPastEnd = 0x40000000u;
   __device__ __forceinline__ void load(int stage, int nst, u32x4 (&v)[kPerWave]) const {
     const int st = __builtin_amdgcn_readfirstlane(stage);
