@@ -61,9 +61,12 @@ __device__ __forceinline__ const uint8_t* group_src(const uint8_t* x, int64_t b,
 }
 
 // Running maximum of |x| into *amax_bits (non-negative binary32 values
-// order like their bit patterns).
+// order like their bit patterns).  512-lane workgroups (at most 512 of
+// them): twice the waves of 256-lane ones for the same number of atomics,
+// which a cold read needs (as for the quantiser's amax pass).
+constexpr int kKvAmaxThreads = 512;
 template <int DTYPE>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kKvAmaxThreads)
 kv_amax_kernel(const uint8_t* __restrict__ x, int64_t ngroups, int64_t kg,
                int64_t ldx_bytes, unsigned* __restrict__ amax_bits) {
   const bool flat = ldx_bytes == kg * 16 * (DTYPE == kDtypeF32 ? 4 : 2);
@@ -78,7 +81,7 @@ kv_amax_kernel(const uint8_t* __restrict__ x, int64_t ngroups, int64_t kg,
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1)
     mx = max(mx, static_cast<unsigned>(__shfl_xor(static_cast<int>(mx), off)));
-  __shared__ unsigned part[4];
+  __shared__ unsigned part[kKvAmaxThreads / 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) part[wave] = mx;
   __syncthreads();
@@ -188,13 +191,14 @@ hipError_t launch_kv_amax_update(const void* x, int x_dtype, int64_t rows, int64
   const int64_t esize = x_dtype == kDtypeF32 ? 4 : 2;
   // at most 512 workgroups, each ending with one atomic on the same word
   // (2048 measured twice as slow on a 32768 x 1024 slab)
-  const unsigned grid = grid_for(ngroups) < 512 ? grid_for(ngroups) : 512;
+  const int64_t want = (ngroups + kKvAmaxThreads - 1) / kKvAmaxThreads;
+  const unsigned grid = static_cast<unsigned>(want < 512 ? want : 512);
   const uint8_t* xb = static_cast<const uint8_t*>(x);
   unsigned* bits = reinterpret_cast<unsigned*>(amax);
   if (x_dtype == kDtypeF32)
-    kv_amax_kernel<0><<<grid, 256, 0, stream>>>(xb, ngroups, kg, ldx * esize, bits);
+    kv_amax_kernel<0><<<grid, kKvAmaxThreads, 0, stream>>>(xb, ngroups, kg, ldx * esize, bits);
   else
-    kv_amax_kernel<1><<<grid, 256, 0, stream>>>(xb, ngroups, kg, ldx * esize, bits);
+    kv_amax_kernel<1><<<grid, kKvAmaxThreads, 0, stream>>>(xb, ngroups, kg, ldx * esize, bits);
   return hipGetLastError();
 }
 

@@ -55,9 +55,13 @@ __global__ void amax_init_kernel(unsigned* bits) { *bits = 0u; }
 
 // max |x| over the tensor: per trip a wave reads 64 consecutive blocks,
 // lane 2j + h half h of blocks j and j + 32 (16 contiguous bytes of bf16 or
-// 32 of fp32 each); one atomic per workgroup
+// 32 of fp32 each); one atomic per workgroup.  Workgroups of 512 lanes: at
+// the cap of 512 workgroups that is 4096 waves, which a cold 335 MB read
+// needs (32768 x 5120 bf16: 50.7 us against 63 us with 256 lanes, the same
+// number of atomics).
+constexpr int kAmaxThreads = 512;
 template <int DTYPE>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kAmaxThreads)
 amax_kernel(const uint8_t* __restrict__ x, int64_t nblocks, int64_t kb,
             int64_t ldx_bytes, unsigned* __restrict__ out_bits) {
   constexpr int kHalfBytes = DTYPE == kDtypeF32 ? 32 : 16;
@@ -80,7 +84,7 @@ amax_kernel(const uint8_t* __restrict__ x, int64_t nblocks, int64_t kb,
   // wave reduction, then one atomic per workgroup
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) mx = max(mx, static_cast<unsigned>(__shfl_xor(static_cast<int>(mx), off)));
-  __shared__ unsigned part[4];
+  __shared__ unsigned part[kAmaxThreads / 64];
   const int wave = threadIdx.x >> 6;
   if (lane == 0) part[wave] = mx;
   __syncthreads();
@@ -111,13 +115,13 @@ hipError_t launch_quantize(const void* x, int x_dtype, int64_t rows,
     unsigned* bits = reinterpret_cast<unsigned*>(global);
     amax_init_kernel<<<1, 1, 0, stream>>>(bits);
     // at most 512 workgroups: each ends with one atomic on the same word, and
-    // more of them (2048) measured slower; 512 x 256 lanes still keep HBM busy
-    const int64_t want = (nblocks + 255) / 256;
+    // more of them (2048) measured slower
+    const int64_t want = (nblocks + kAmaxThreads - 1) / kAmaxThreads;
     const unsigned grid = static_cast<unsigned>(want < 512 ? want : 512);
     if (x_dtype == kDtypeF32)
-      amax_kernel<0><<<grid, 256, 0, stream>>>(xb, nblocks, kb, ldx_bytes, bits);
+      amax_kernel<0><<<grid, kAmaxThreads, 0, stream>>>(xb, nblocks, kb, ldx_bytes, bits);
     else
-      amax_kernel<1><<<grid, 256, 0, stream>>>(xb, nblocks, kb, ldx_bytes, bits);
+      amax_kernel<1><<<grid, kAmaxThreads, 0, stream>>>(xb, nblocks, kb, ldx_bytes, bits);
     amax_finalize_kernel<<<1, 1, 0, stream>>>(global);
   }
   // one block per lane (a one-shot grid measured faster than a resident
