@@ -142,20 +142,32 @@ dequantize_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__
   }
 }
 
-// 16 input values of a block as binary32 (exact from bf16 or fp32).
+// A block's raw input bytes (bf16: 32 bytes, fp32: 64) and its values as
+// binary32 (exact from bf16 or fp32).
 template <int DTYPE>
-__device__ __forceinline__ void load_values(const uint8_t* src, float* x) {
+struct RawX {
+  static constexpr int kVec = DTYPE == kDtypeF32 ? 4 : 2;
+  uint4 q[kVec];
+};
+
+template <int DTYPE>
+__device__ __forceinline__ void load_raw(const uint8_t* src, RawX<DTYPE>& r) {
+#pragma unroll
+  for (int i = 0; i < RawX<DTYPE>::kVec; ++i) r.q[i] = reinterpret_cast<const uint4*>(src)[i];
+}
+
+template <int DTYPE>
+__device__ __forceinline__ void raw_values(const RawX<DTYPE>& r, float* x) {
   if constexpr (DTYPE == kDtypeF32) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float4 t = reinterpret_cast<const float4*>(src)[q];
-      x[4 * q] = t.x; x[4 * q + 1] = t.y; x[4 * q + 2] = t.z; x[4 * q + 3] = t.w;
+      x[4 * q] = __uint_as_float(r.q[q].x); x[4 * q + 1] = __uint_as_float(r.q[q].y);
+      x[4 * q + 2] = __uint_as_float(r.q[q].z); x[4 * q + 3] = __uint_as_float(r.q[q].w);
     }
   } else {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const uint4 t = reinterpret_cast<const uint4*>(src)[q];
-      const unsigned w[4] = {t.x, t.y, t.z, t.w};
+      const unsigned w[4] = {r.q[q].x, r.q[q].y, r.q[q].z, r.q[q].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         x[8 * q + 2 * i] = __uint_as_float(w[i] << 16);
@@ -165,8 +177,12 @@ __device__ __forceinline__ void load_values(const uint8_t* src, float* x) {
   }
 }
 
-// One wave per row: lane l takes blocks l, l + 64, ...; float64 sums are
-// reduced across the wave.  stats[row] = {sum x^2, sum (x - x_hat)^2, max|x|}.
+// One wave per row: lane l takes blocks l, l + 64, ..., kBatch of them at a
+// time, all of a batch's loads issued before any of its arithmetic (a row's
+// blocks one after the other left each wave waiting on memory once per
+// block); float64 sums, per lane in block order, are reduced across the
+// wave.  stats[row] = {sum x^2, sum (x - x_hat)^2, max|x|}.
+constexpr int kStatsBatch = 4;
 template <int DTYPE>
 __global__ void __launch_bounds__(256)
 error_stats_kernel(const uint8_t* __restrict__ x, int64_t rows, int64_t kb,
@@ -178,23 +194,39 @@ error_stats_kernel(const uint8_t* __restrict__ x, int64_t rows, int64_t kb,
   const int64_t row = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (row >= rows) return;   // whole waves leave together
   const double g = static_cast<double>(*global);
+  const uint8_t* const xrow = x + row * ldx_bytes;
+  const int64_t blk0 = row * kb;
   double sx = 0.0, se = 0.0;
   unsigned mx = 0u;
-  for (int64_t b = lane; b < kb; b += 64) {
-    float xv[16], v[16];
-    load_values<DTYPE>(x + row * ldx_bytes + b * (16 * kElemBytes), xv);
-    const int64_t blk = row * kb + b;
-    decode_block(reinterpret_cast<const uint2*>(codes)[blk], e4m3_f32(scales[blk]), v);
+  for (int64_t b0 = lane; b0 < kb; b0 += 64 * kStatsBatch) {
+    RawX<DTYPE> raw[kStatsBatch];
+    uint2 cw[kStatsBatch];
+    unsigned sb[kStatsBatch];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const double xd = static_cast<double>(xv[i]);
-      // v * g is exact in float64 (at most 6 + 24 significant bits), so the
-      // fused form rounds x - v g once, as the separate product and
-      // difference do: the same value in one float64 operation fewer
-      const double d = __builtin_fma(-static_cast<double>(v[i]), g, xd);
-      sx = __builtin_fma(xd, xd, sx);
-      se = __builtin_fma(d, d, se);
-      mx = max(mx, __float_as_uint(xv[i]) & 0x7FFFFFFFu);
+    for (int u = 0; u < kStatsBatch; ++u) {
+      const int64_t b = b0 + 64 * u;
+      const int64_t bb = b < kb ? b : kb - 1;   // past the row: a valid block, not counted
+      load_raw<DTYPE>(xrow + bb * (16 * kElemBytes), raw[u]);
+      cw[u] = reinterpret_cast<const uint2*>(codes)[blk0 + bb];
+      sb[u] = scales[blk0 + bb];
+    }
+#pragma unroll
+    for (int u = 0; u < kStatsBatch; ++u) {
+      if (b0 + 64 * u >= kb) break;
+      float xv[16], v[16];
+      raw_values<DTYPE>(raw[u], xv);
+      decode_block(cw[u], e4m3_f32(sb[u]), v);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const double xd = static_cast<double>(xv[i]);
+        // v * g is exact in float64 (at most 6 + 24 significant bits), so the
+        // fused form rounds x - v g once, as the separate product and
+        // difference do: the same value in one float64 operation fewer
+        const double d = __builtin_fma(-static_cast<double>(v[i]), g, xd);
+        sx = __builtin_fma(xd, xd, sx);
+        se = __builtin_fma(d, d, se);
+        mx = max(mx, __float_as_uint(xv[i]) & 0x7FFFFFFFu);
+      }
     }
   }
 #pragma unroll
