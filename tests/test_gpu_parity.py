@@ -431,7 +431,10 @@ STREAM_SHAPES = [(7, 4109, 512),      # S rows per workgroup 24, L 16
                  (12000, 40, 512),    # S = A: 64, L 64, 512-K stages
                  (20000, 64, 512),    # S = A: 128, L 64, 256-K stages
                  (20000, 32, 512),    # S = A: 128, L 32
-                 (4100, 8, 1024)]     # S = A: 24, L 16
+                 (4100, 8, 1024),     # S = A: 24, L 16
+                 (5, 40, 1024),       # both small: L = A (5 rows), one 40-row S slice
+                 (64, 64, 512),       # both 64: L = A, 512-K stages for 64-row L
+                 (1, 3, 512)]         # one output row, three columns
 
 
 @pytest.mark.parametrize("m,n,k", STREAM_SHAPES)
@@ -690,7 +693,8 @@ def _gate_params(n_alpha, seed):
                                                 (70, 128, 128, 640),
                                                 (1000, 64, 64, 512), (20000, 64, 64, 256),
                                                 (33, 0, 40, 512), (5000, 20, 12, 1024),
-                                                (3000, 60, 4, 256), (4100, 7, 9, 512)])
+                                                (3000, 60, 4, 256), (4100, 7, 9, 512),
+                                                (1, 8, 8, 512), (2, 0, 64, 1024)])
 def test_gdn_gates(m, n_beta, n_alpha, k):
     rng = np.random.default_rng(m + n_beta + 3 * n_alpha + k)
     xv = rng.standard_normal((m, k)).astype(np.float32)
